@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library, loaded; skips when there is no GPU."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_deltanet_prefill_amd as gdn
+    gdn.load()
+    return gdn
