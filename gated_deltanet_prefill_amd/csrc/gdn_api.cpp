@@ -1,0 +1,128 @@
+// gdn_api.cpp -- the C ABI of libgdn: argument checks, then one launch.
+//
+// Every check runs on the host before anything touches the device, so an
+// invalid call returns its error code with no output written (the ferrox-core
+// gdn_chunk.rs page's convention that a failed call leaves the state
+// untouched, without that page's host fallback).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;                 // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void *p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, p ? a + (uintptr_t)bytes : a};
+}
+
+bool overlap(Range a, Range b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+int elem_size(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
+
+// Shared checks of both entry points; T = 1 for the step.
+int check(const void *q, const void *k, const void *v, const float *g,
+          const float *beta, const float *state_in, const float *state_out,
+          const void *y, long B, long T, long Hk, long Hv, long Dk, long Dv,
+          int dtype)
+{
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0) return GDN_ERR_SHAPE;
+    if (Hv % Hk != 0) return GDN_ERR_SHAPE;
+    if (B * Hv * (Dv / 32 > 0 ? Dv / 32 : 1) > INT32_MAX) return GDN_ERR_SHAPE;
+    if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_F16) return GDN_ERR_DTYPE;
+    if (!supported_dim((int)Dk) || !supported_dim((int)Dv)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    if (!state_out) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
+    const void *p16[] = {q, k, v, y, state_in, state_out};
+    for (const void *p : p16)
+        if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
+    if ((g && !aligned(g, 4)) || (beta && !aligned(beta, 4))) return GDN_ERR_ALIGN;
+
+    const uint64_t es = (uint64_t)elem_size(dtype);
+    const uint64_t nqk = (uint64_t)B * T * Hk * Dk, nv = (uint64_t)B * T * Hv * Dv;
+    const uint64_t ngb = (uint64_t)B * T * Hv, ns = (uint64_t)B * Hv * Dv * Dk;
+    const Range rq = range_of(T ? q : nullptr, nqk * es), rk = range_of(T ? k : nullptr, nqk * es);
+    const Range rv = range_of(T ? v : nullptr, nv * es), ry = range_of(T ? y : nullptr, nv * es);
+    const Range rg = range_of(T ? g : nullptr, ngb * 4), rb = range_of(T ? beta : nullptr, ngb * 4);
+    const Range rsi = range_of(state_in, ns * 4), rso = range_of(state_out, ns * 4);
+    // y overlaps nothing; state_out overlaps nothing but (exactly) state_in
+    const Range others_y[] = {rq, rk, rv, rg, rb, rsi, rso};
+    for (const Range &r : others_y)
+        if (overlap(ry, r)) return GDN_ERR_ALIAS;
+    const Range others_s[] = {rq, rk, rv, rg, rb};
+    for (const Range &r : others_s)
+        if (overlap(rso, r)) return GDN_ERR_ALIAS;
+    if (state_in && state_in != state_out && overlap(rsi, rso)) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta,
+                  const float *state_in, float *state_out, void *y,
+                  int B, int T, int Hk, int Hv, int Dk, int Dv, int C,
+                  gdn_dtype dtype, hipStream_t stream)
+{
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    if (rc != GDN_OK) return rc;
+    if (C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
+                   B, T, Hk, Hv, Dk, Dv, C, (float)(1.0 / sqrt((double)Dk))};
+    hipError_t e;
+    switch (dtype) {
+    case GDN_F32: e = gdn::launch_chunk_f32(a, stream); break;
+    case GDN_BF16: e = gdn::launch_chunk_bf16(a, stream); break;
+    default: e = gdn::launch_chunk_f16(a, stream); break;
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_step(const void *q, const void *k, const void *v,
+             const float *g, const float *beta,
+             const float *state_in, float *state_out, void *y,
+             int B, int Hk, int Hv, int Dk, int Dv,
+             gdn_dtype dtype, hipStream_t stream)
+{
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, 1, Hk, Hv, Dk, Dv, (int)dtype);
+    if (rc != GDN_OK) return rc;
+    if (B == 0) return GDN_OK;
+    gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
+                   B, 1, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk))};
+    hipError_t e = gdn::launch_step((int)dtype, a, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid shape (negative size, or Hv not a multiple of Hk)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be 32, 64 or 128; C must be 16, 32 or 64)";
+    case GDN_ERR_ALIAS: return "an output overlaps another buffer";
+    case GDN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, y, state; 4 for g, beta)";
+    case GDN_ERR_HIP: return "HIP launch failed";
+    case GDN_ERR_DTYPE: return "unknown dtype";
+    default: return "unknown status";
+    }
+}
+
+int gdn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// gdn_internal.h -- launchers shared between the kernel units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace gdn {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *state_in;
+    float *state_out;
+    void *y;
+    int B, T, Hk, Hv, Dk, Dv, C;
+    float scale;
+};
+
+// Each returns hipSuccess or the launch error; arguments are already valid.
+hipError_t launch_chunk_f32(const FwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_f16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_step(int dtype, const FwdArgs &a, hipStream_t s);
+
+// Largest chunk the float32 path can hold in LDS; bigger requests run with
+// this chunk length (the result does not depend on the chunk length).
+constexpr int kMaxChunkF32 = 32;
+
+}  // namespace gdn

@@ -1,0 +1,127 @@
+/*
+ * gdn.h -- C ABI of the gated delta rule (gated DeltaNet) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Per batch b and value head hv, with k-head hk = hv / (Hv/Hk)
+ * (the grouped head map of the metaltile-std gated_delta_wy.rs page,
+ * "Layouts"), a state S of Dv x Dk float32 advances over tokens t:
+ *
+ *     d_t = beta_t * (v_t - g_t * S_{t-1} k_t)
+ *     S_t = g_t * S_{t-1} + d_t k_t^T
+ *     y_t = S_t q_t / sqrt(Dk)
+ *
+ * (the rule as stated on the ferrox-core gdn_chunk.rs page, "The algebra",
+ * with g_t the decay that multiplies the state -- not its logarithm -- and
+ * the output read from the updated state and scaled by 1/sqrt(Dk)).
+ *
+ * Layouts (dense, contiguous, row-major; metaltile-std page, "Layouts"):
+ *     q, k      [B, T, Hk, Dk]     dtype
+ *     v, y      [B, T, Hv, Dv]     dtype
+ *     g, beta   [B, T, Hv]         float32
+ *     state     [B, Hv, Dv, Dk]    float32 (row j = value index j)
+ *
+ * Ownership and execution.  Every pointer is device memory owned by the
+ * caller (for example from torch on ROCm).  The library allocates nothing,
+ * keeps no state between calls and is thread-safe.  Work is enqueued on
+ * `stream` (NULL = the default stream) without host synchronisation; the
+ * outputs are valid once the stream reaches that point.
+ *
+ * Errors.  All arguments are checked on the host before anything is
+ * enqueued; on any GDN_ERR_* other than GDN_ERR_HIP nothing is launched and
+ * no output is touched.  GDN_ERR_HIP means a launch failed; the outputs are
+ * then undefined.  There is no host fallback.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, k, v and y.  g, beta and the state are always float32. */
+typedef enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_BF16 = 1,
+    GDN_F16 = 2
+} gdn_dtype;
+
+enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    GDN_ERR_SHAPE = -2,       /* negative size, or Hv not a multiple of Hk   */
+    GDN_ERR_UNSUPPORTED = -3, /* Dk, Dv or C outside the supported set       */
+    GDN_ERR_ALIAS = -4,       /* an output overlaps another buffer           */
+    GDN_ERR_ALIGN = -5,       /* a pointer is not 16-byte (4 for g, beta) aligned */
+    GDN_ERR_HIP = -6,         /* a HIP launch failed                         */
+    GDN_ERR_DTYPE = -7        /* dtype is not a gdn_dtype value              */
+};
+
+/*
+ * gdn_chunk_fwd -- T tokens of the rule, processed in chunks of C tokens,
+ * with the state read once from state_in and written once to state_out.
+ *
+ * The chunked computation is the one the metaltile-std gated_delta_wy.rs page
+ * describes ("Algorithm": gates, K K^T, the unit lower triangular system,
+ * the chunk's outputs and the chunk-end state) and the ferrox-core
+ * gdn_chunk.rs page derives ("The algebra": every decay ratio a product of
+ * decays, never a quotient).  It equals the sequential rule above up to
+ * float association; C changes speed, not the result.
+ *
+ *   q, k        [B,T,Hk,Dk] dtype, 16-byte aligned.
+ *   v           [B,T,Hv,Dv] dtype, 16-byte aligned.
+ *   g, beta     [B,T,Hv] float32, 4-byte aligned.  g is the decay value.
+ *   state_in    [B,Hv,Dv,Dk] float32, 16-byte aligned, or NULL for a zero
+ *               initial state.
+ *   state_out   [B,Hv,Dv,Dk] float32, 16-byte aligned.  May equal state_in
+ *               (in-place update); any other overlap is GDN_ERR_ALIAS.
+ *   y           [B,T,Hv,Dv] dtype, 16-byte aligned; must not overlap any
+ *               other buffer.
+ *   B, T        batch and tokens; B = 0 is a no-op, T = 0 copies the initial
+ *               state (or zeros) to state_out and writes no y (q, k, v, g,
+ *               beta and y may then be NULL).
+ *   Hk, Hv      key and value heads, Hv % Hk == 0.
+ *   Dk, Dv      head dimensions, each one of 32, 64, 128.
+ *   C           chunk length, one of 16, 32, 64 (the tail chunk of
+ *               T - C*floor(T/C) tokens is handled inside the kernel).
+ *   dtype       storage type of q, k, v, y.
+ *   stream      HIP stream (NULL = default stream).
+ * Returns GDN_OK or a GDN_ERR_* code.
+ */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta,
+                  const float *state_in, float *state_out, void *y,
+                  int B, int T, int Hk, int Hv, int Dk, int Dv, int C,
+                  gdn_dtype dtype, hipStream_t stream);
+
+/*
+ * gdn_step -- one token of the rule (decode): each state row is read once
+ * and written once (the sequential step of the ferrox-core gdn_chunk.rs
+ * page, "Why": the step is bound by the state traffic).
+ *
+ *   q, k        [B,Hk,Dk] dtype (the T = 1 case of the layouts above).
+ *   v, y        [B,Hv,Dv] dtype.
+ *   g, beta     [B,Hv] float32.
+ *   state_in    [B,Hv,Dv,Dk] float32 or NULL (zero state).
+ *   state_out   [B,Hv,Dv,Dk] float32; may equal state_in (in place).
+ *   Other arguments, alignment and errors as for gdn_chunk_fwd; Dk and Dv
+ *   each one of 32, 64, 128.
+ */
+int gdn_step(const void *q, const void *k, const void *v,
+             const float *g, const float *beta,
+             const float *state_in, float *state_out, void *y,
+             int B, int Hk, int Hv, int Dk, int Dv,
+             gdn_dtype dtype, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *gdn_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */
