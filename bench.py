@@ -1,0 +1,341 @@
+#!/usr/bin/env python
+"""Throughput of the gated delta rule forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one ``gdn_chunk_fwd`` over the long-prefill workload (B=8,
+T=8192, Hk=16, Hv=32, Dk=Dv=128, C=64, bf16 q/k/v/y, f32 g/beta/state), with
+seeded synthetic inputs already resident in HBM.  W untimed steps, then K
+timed steps bracketed by ``torch.cuda.synchronize()``.  One JSON line is
+printed with:
+
+* ``value``       prefill tokens/s (B*T per step);
+* ``roofline``    the chunk kernel against the HBM roofline (it is
+                  bandwidth-bound at this intensity): algorithmic bytes per
+                  launch / average launch time (HIP events on the launch
+                  stream), against 8 TB/s; ``traffic`` is the measured HBM
+                  bytes per launch from the committed counter summary when it
+                  was taken on the current kernel source, else null;
+* ``roofline_mfma`` the same launch as algorithmic FLOP/s against the dense
+                  bf16 MFMA peak;
+* ``decode``      256 chained ``gdn_step`` launches on the decode workload
+                  (B=64, Hk=16, Hv=32, Dk=Dv=128, fp16 I/O, f32 state in
+                  place): state GB/s and total GB/s against 8 TB/s;
+* ``cpu_baseline`` the float64 CPU oracle timed on a bounded sample of the
+                  same workload (4 of the 8 batch elements: all heads, all
+                  8192 tokens), with the thread count it used.
+
+``--copy-calibration N`` instead times a plain device copy of N MiB (used to
+scale the HBM byte counters); it prints its own JSON line.
+
+``--summarize-traffic FETCH WRITE COPY_FETCH COPY_WRITE`` reads four
+``rocprofv3 --pmc ... --output-format csv`` result directories (FETCH_SIZE and
+WRITE_SIZE of a bench run, and of a ``--copy-calibration 1024`` run), scales
+each counter by what it reads for the copy of known size, and writes the
+measured HBM bytes per chunk launch to ``profiles/`` together with a hash of
+the chunk kernel's source (the figure is only reported for that source).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + TFLOP/s (chunk) and state GB/s (step), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, TFLOP/s
+PREFILL = dict(B=8, T=8192, Hk=16, Hv=32, Dk=128, Dv=128, C=64, dtype="bf16")
+DECODE = dict(B=64, T=256, Hk=16, Hv=32, Dk=128, Dv=128, dtype="f16")
+CHUNK_KERNEL_SOURCES = ["gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_device.h",
+                        "gdn_chunk_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_long_prefill_hbm_traffic.json")
+
+
+def chunk_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in CHUNK_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_prefill_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_bytes(B, T, Hk, Hv, Dk, Dv, es=2, **_):
+    """Algorithmic HBM bytes of one launch: q, k once per key head, v, y,
+    g, beta, and the state read once and written once."""
+    return (2 * B * T * Hk * Dk * es + 2 * B * T * Hv * Dv * es + 2 * B * T * Hv * 4
+            + 2 * B * Hv * Dv * Dk * 4)
+
+
+def prefill_flops(B, T, Hv, Dk, Dv, C, **_):
+    """Algorithmic FLOPs: per token and value head, the three state-sized
+    products (6 Dk Dv), the causal halves of K K^T and Q K^T (2 C Dk) and the
+    value-side solve plus the intra-chunk term (2 C Dv)."""
+    return B * T * Hv * (6 * Dk * Dv + 2 * C * Dk + 2 * C * Dv)
+
+
+def step_bytes(B, Hk, Hv, Dk, Dv, es=2, **_):
+    state = 2 * B * Hv * Dv * Dk * 4
+    return state, state + 2 * B * Hk * Dk * es + 2 * B * Hv * Dv * es + 2 * B * Hv * 4
+
+
+def load_traffic():
+    """Measured HBM bytes per chunk launch, if taken on the current source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != chunk_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _counter_means(result_dir, counter):
+    """Mean counter value per kernel name from a rocprofv3 csv directory."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(result_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def summarize_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib=1024):
+    kib = copy_mib * 1024.0
+
+    def pick(means, needle):
+        hits = [v for k, v in means.items() if needle in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {needle!r} in counter results")
+        return max(hits)
+
+    copy_fetch = pick(_counter_means(cfetch_dir, "FETCH_SIZE"), "copyBuffer")
+    copy_write = pick(_counter_means(cwrite_dir, "WRITE_SIZE"), "copyBuffer")
+    f_scale, w_scale = kib / copy_fetch, kib / copy_write
+    fetch = pick(_counter_means(fetch_dir, "FETCH_SIZE"), "chunk_fwd_kernel")
+    write = pick(_counter_means(write_dir, "WRITE_SIZE"), "chunk_fwd_kernel")
+    rec = {
+        "kernel": "chunk_fwd_kernel<bf16,128,128,64>, long prefill",
+        "source_hash": chunk_source_hash(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "copy_calibration_mib": copy_mib,
+        "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "read_bytes_per_launch": fetch * f_scale * 1024,
+        "write_bytes_per_launch": write * w_scale * 1024,
+        "bytes_per_launch": (fetch * f_scale + write * w_scale) * 1024,
+        "algorithmic_bytes_per_launch": prefill_bytes(**PREFILL),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    ev0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": ms, "GB/s": 2 * n * 4 / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
+              "slot is independent, so more GPUs would each run this same kernel on their share.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_prefill_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def upload(arr, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    # ---------------- prefill
+    P = PREFILL
+    inp = gi.workload_inputs("long_prefill")
+    q, k, v = (upload(inp[n], "bf16") for n in ("q", "k", "v"))
+    g, beta = upload(inp["g"], "f32"), upload(inp["beta"], "f32")
+    s_in = upload(inp["state"], "f32")
+    s_out = torch.empty_like(s_in)
+    y = torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.chunk_fwd(q, k, v, g, beta, s_in, C=P["C"], state_out=s_out, y=y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    tokens = P["B"] * P["T"]
+    nbytes = prefill_bytes(**P)
+    nflops = prefill_flops(**P)
+    achieved_gbs = nbytes / avg_launch_s / 1e9
+    traffic = load_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g U[0.95,1), "
+                "beta sigmoid(N(0,1)), state N(0,0.05))",
+        "config": {"workload": "long_prefill", "B": P["B"], "T": P["T"], "Hk": P["Hk"],
+                   "Hv": P["Hv"], "Dk": P["Dk"], "Dv": P["Dv"], "C": P["C"]},
+        "roofline": {
+            "kernel": "chunk_fwd_kernel<bf16,128,128,64>",
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_us_avg": avg_launch_s * 1e6,
+            "launch_us_min": min(launch_ms) * 1e3,
+        },
+        "roofline_mfma": {
+            "achieved": nflops / avg_launch_s / 1e12,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": nflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": nflops,
+        },
+    }
+    del q, k, v, g, beta, y, s_out
+    torch.cuda.empty_cache()
+
+    # ---------------- decode
+    if not args.no_decode:
+        D = DECODE
+        dinp = gi.workload_inputs("decode")
+        dq, dk, dv = (upload(dinp[n], "f16") for n in ("q", "k", "v"))
+        dg, db = upload(dinp["g"], "f32"), upload(dinp["beta"], "f32")
+        st0 = upload(dinp["state"], "f32")
+        nsteps = min(args.decode_steps, D["T"])
+        toks = [tuple(t[:, i].contiguous() for t in (dq, dk, dv, dg, db)) for i in range(nsteps)]
+        ys = [torch.empty((D["B"], D["Hv"], D["Dv"]), dtype=torch.float16, device=dev)
+              for _ in range(nsteps)]
+        st = st0.clone()
+
+        def run_decode():
+            for i in range(nsteps):
+                gdn.step(*toks[i], st, state_out=st, y=ys[i], stream=stream)
+
+        run_decode()
+        st.copy_(st0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_decode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_step = e0.elapsed_time(e1) * 1e3 / nsteps
+        sbytes, tbytes = step_bytes(**D)
+        out["decode"] = {
+            "workload": "decode", "B": D["B"], "Hk": D["Hk"], "Hv": D["Hv"], "Dk": D["Dk"],
+            "Dv": D["Dv"], "dtype": "f16", "chained_steps": nsteps,
+            "us_per_step": us_step,
+            "state_GBps": sbytes / (us_step * 1e-6) / 1e9,
+            "total_GBps": tbytes / (us_step * 1e-6) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": tbytes / (us_step * 1e-6) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": tbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "launches": "plain back-to-back launches, state updated in place",
+            "note": "the 128 MiB state fits in the 256 MB last-level cache between steps",
+        }
+        del toks, ys, st, st0, dq, dk, dv, dg, db
+
+    # ---------------- CPU oracle on a bounded sample
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = len(os.sched_getaffinity(0))
+        nb = 4                                   # 4 of the 8 batch elements
+        qs, ks, vs = (gi.decode(inp[n][:nb], "bf16") for n in ("q", "k", "v"))
+        gs, bs = inp["g"][:nb].astype(np.float64), inp["beta"][:nb].astype(np.float64)
+        ss = inp["state"][:nb].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.forward(qs, ks, vs, gs, bs, ss, nthreads=nthreads)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": nb * P["T"] / cpu_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nb} of the {P['B']} batch elements of the long prefill: {nb} x {P['T']} "
+                      f"tokens x {P['Hv']} value heads (float64 sequential rule, OpenMP over "
+                      f"(batch, head) slots), {cpu_s:.2f} s",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/gdn.h"
+#include "gdn.h"
 #include "gdn_internal.h"
 
 namespace {

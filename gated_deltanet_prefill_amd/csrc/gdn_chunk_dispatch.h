@@ -12,11 +12,14 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
     constexpr int DVS = DV;                      // one workgroup per slot
     using L = ChunkCfg<ET, DK, DVS, C, NB>;
     const int nsplit = DV / DVS;
-    const dim3 grid((unsigned)a.B * (unsigned)a.Hv * (unsigned)nsplit), block(L::NT);
+    const long nblocks = (long)a.B * a.Hv * nsplit;
+    const int group = a.Hv / a.Hk;
+    const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
+    const dim3 grid((unsigned)nblocks), block(L::NT);
     hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), grid, block, 0, st,
                        static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                        static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, a.scale);
+                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale);
     return hipGetLastError();
 }
 

@@ -54,7 +54,8 @@ struct ChunkCfg {
     static constexpr int NBK = DK / 16;               // 16-wide key blocks
     static constexpr int EPU = 16 / (int)sizeof(ET);  // elements per 16-byte unit
     static constexpr int LDK = DK + EPU;              // row stride of sK, sQ
-    static constexpr int LDC = C + EPU;               // row stride of sKt, sVt, sT1, sT2, sQKR
+    static constexpr int LDC = C + 4;                 // row stride of sKt, sVt, sT1, sT2, sQKR
+                                                      // (odd multiple of 8 bytes / bank group)
     static constexpr int LDF = C + 4;                 // row stride of f32 C x C matrices
     static constexpr int ES = (int)sizeof(ET);
     static constexpr int oK = 0;
@@ -72,7 +73,6 @@ struct ChunkCfg {
     static constexpr int BYTES = oVec + 8 * C * 4;
     static constexpr int NPAIR = NBT * (NBT + 1) / 2;   // lower block tiles of C x C
     static constexpr int NTILE = 2 * NPAIR;             // K K^T and Q K^T tiles
-    static constexpr int MAXT = (NTILE + NW - 1) / NW;  // tiles per wave
     // staging: 16-byte units
     static constexpr int UPK = DK / EPU;                // units per K / Q row
     static constexpr int UPV = DVS / EPU;               // units per V row (slice)
@@ -131,13 +131,21 @@ template <typename ET> union Unit16 {
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then for every wave.  Unlike __syncthreads() it does not wait
+// for outstanding global loads and stores, so the next chunk's prefetch and
+// this chunk's y stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename ET, int DK, int DVS, int C, int NB>
 __global__ __launch_bounds__(4 * DVS / NB, 1)
 void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                       const ET *__restrict__ v, const float *__restrict__ g,
                       const float *__restrict__ beta, const float *state_in,
                       float *state_out, ET *__restrict__ y,
-                      int T, int Hk, int Hv, int Dv, int nsplit, float scale)
+                      int T, int Hk, int Hv, int Dv, int nsplit, int xcd_group, float scale)
 {
     using L = ChunkCfg<ET, DK, DVS, C, NB>;
     using X4 = typename Vec<ET>::x4;
@@ -168,7 +176,17 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, x = lane & 15, qd = lane >> 4;
-    const int slot = blockIdx.x / nsplit, vs = blockIdx.x - slot * nsplit;
+    // Workgroups are dealt round-robin over the 8 XCDs, so workgroups i and
+    // i + 8 share an XCD and its L2.  With xcd_group = Hv/Hk > 1 they get
+    // value heads of the same key head, whose q/k stream is then fetched
+    // from HBM once per group instead of once per head.
+    int bid = blockIdx.x;
+    if (xcd_group > 1) {
+        const int xcd = bid & 7, kk = bid >> 3;
+        const int sib = kk % xcd_group, m = kk / xcd_group;
+        bid = (m * 8 + xcd) * xcd_group + sib;
+    }
+    const int slot = bid / nsplit, vs = bid - slot * nsplit;
     const int hv = slot % Hv, b = slot / Hv, hk = hv / (Hv / Hk);
     const int vloc = wave * 16 * NB;               // first slice column of this wave
 
@@ -183,12 +201,22 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + 16 * kb + 4 * qd)
                                  : zero4();
     }
+    // Consume the loaded state here, before the chunk loop, so that no load
+    // is still pending at the loop header (where a wait would otherwise be
+    // placed on every iteration).
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
 
     // ---- structural zeros of the C x C matrices (upper triangles never written)
     for (int i = tid; i < (L::oRin - L::oT1) / 16; i += NT)
         reinterpret_cast<uint4 *>(smem + L::oT1)[i] = zero_u4();
 
-    // ---- global -> register prefetch of one chunk
+    // ---- global -> register prefetch of one chunk.  Every load is issued
+    // unconditionally from a clamped (always valid) row; rows past the end
+    // of the sequence are zeroed when the registers are staged, so nothing
+    // consumes the loaded values before the next chunk's staging point.
     const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * Dv;
     const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
     const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
@@ -199,57 +227,67 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     uint4 rk[L::PERK][4], rq[L::PERQ], rv[L::PERV][4];
     float rg = 1.f, rb = 0.f;
     auto prefetch = [&](int t0) {
-        const int cn = min(C, T - t0);
+        const int last = min(C, T - t0) - 1;
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
-            const int it = tid + i * NT;
+            const int it = min(tid + i * NT, L::KIT - 1);
             const int rgp = it / L::UPK, u = it - rgp * L::UPK;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 4 * rgp + r;
-                rk[i][r] = (it < L::KIT && t < cn)
-                    ? *reinterpret_cast<const uint4 *>(kbase + (size_t)(t0 + t) * kstride + u * EPU)
-                    : zero_u4();
+                const int t = min(4 * rgp + r, last);
+                rk[i][r] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(t0 + t) * kstride + u * EPU);
             }
         }
 #pragma unroll
         for (int i = 0; i < L::PERQ; ++i) {
-            const int it = tid + i * NT;
-            const int t = it / L::UPK, u = it - t * L::UPK;
-            rq[i] = (it < L::QIT && t < cn)
-                ? *reinterpret_cast<const uint4 *>(qbase + (size_t)(t0 + t) * kstride + u * EPU)
-                : zero_u4();
+            const int it = min(tid + i * NT, L::QIT - 1);
+            const int t = min(it / L::UPK, last), u = it % L::UPK;
+            rq[i] = *reinterpret_cast<const uint4 *>(qbase + (size_t)(t0 + t) * kstride + u * EPU);
         }
 #pragma unroll
         for (int i = 0; i < L::PERV; ++i) {
-            const int it = tid + i * NT;
+            const int it = min(tid + i * NT, L::VIT - 1);
             const int rgp = it / L::UPV, u = it - rgp * L::UPV;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 4 * rgp + r;
-                rv[i][r] = (it < L::VIT && t < cn)
-                    ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(t0 + t) * vstride + u * EPU)
-                    : zero_u4();
+                const int t = min(4 * rgp + r, last);
+                rv[i][r] = *reinterpret_cast<const uint4 *>(vbase + (size_t)(t0 + t) * vstride + u * EPU);
             }
         }
-        if (tid < C) {
-            const bool in = tid < cn;
-            rg = in ? gbase[(size_t)(t0 + tid) * Hv] : 1.f;
-            rb = in ? bbase[(size_t)(t0 + tid) * Hv] : 0.f;
-        }
+        const int tg = min(tid, last);
+        rg = gbase[(size_t)(t0 + tg) * Hv];
+        rb = bbase[(size_t)(t0 + tg) * Hv];
     };
 
-    auto stage = [&]() {
+    // Registers -> LDS: K row-major and transposed, Q, the V slice
+    // transposed, g and beta; rows t >= cn become k = q = v = 0, g = 1,
+    // beta = 0.  The empty asm statements pin the point where the prefetched
+    // values are first needed here, after the barrier.
+    auto stage = [&](int cn, float &gcur, float &bcur) {
+#pragma unroll
+        for (int i = 0; i < L::PERK; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asm volatile("" : "+v"(rk[i][r].x), "+v"(rk[i][r].y), "+v"(rk[i][r].z), "+v"(rk[i][r].w));
+#pragma unroll
+        for (int i = 0; i < L::PERQ; ++i)
+            asm volatile("" : "+v"(rq[i].x), "+v"(rq[i].y), "+v"(rq[i].z), "+v"(rq[i].w));
+#pragma unroll
+        for (int i = 0; i < L::PERV; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asm volatile("" : "+v"(rv[i][r].x), "+v"(rv[i][r].y), "+v"(rv[i][r].z), "+v"(rv[i][r].w));
+        asm volatile("" : "+v"(rg), "+v"(rb));
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
             const int it = tid + i * NT;
-            if (it < L::KIT) {
+            if (L::KIT % NT == 0 || it < L::KIT) {
                 const int rgp = it / L::UPK, u = it - rgp * L::UPK;
                 Unit16<ET> w[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    w[r].u = rk[i][r];
-                    *reinterpret_cast<uint4 *>(sK + (4 * rgp + r) * LDK + u * EPU) = rk[i][r];
+                    w[r].u = (4 * rgp + r < cn) ? rk[i][r] : zero_u4();
+                    *reinterpret_cast<uint4 *>(sK + (4 * rgp + r) * LDK + u * EPU) = w[r].u;
                 }
 #pragma unroll
                 for (int e = 0; e < EPU; ++e) {
@@ -262,19 +300,19 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
         for (int i = 0; i < L::PERQ; ++i) {
             const int it = tid + i * NT;
-            if (it < L::QIT) {
+            if (L::QIT % NT == 0 || it < L::QIT) {
                 const int t = it / L::UPK, u = it - t * L::UPK;
-                *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = rq[i];
+                *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = (t < cn) ? rq[i] : zero_u4();
             }
         }
 #pragma unroll
         for (int i = 0; i < L::PERV; ++i) {
             const int it = tid + i * NT;
-            if (it < L::VIT) {
+            if (L::VIT % NT == 0 || it < L::VIT) {
                 const int rgp = it / L::UPV, u = it - rgp * L::UPV;
                 Unit16<ET> w[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) w[r].u = rv[i][r];
+                for (int r = 0; r < 4; ++r) w[r].u = (4 * rgp + r < cn) ? rv[i][r] : zero_u4();
 #pragma unroll
                 for (int e = 0; e < EPU; ++e) {
                     X4 col;
@@ -283,66 +321,82 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         }
-        if (tid < C) {
-            sg[tid] = rg;
-            sb[tid] = rb;
-        }
+        gcur = (tid < cn) ? rg : 1.f;
+        bcur = (tid < cn) ? rb : 0.f;
+        if (tid < C) sb[tid] = bcur;
     };
 
+    // Which wave computes shared K K^T / Q K^T tile number cnt: with four or
+    // more waves, wave 0 (which also forms the gate products) is skipped.
+    constexpr int TW0 = NW >= 4 ? 1 : 0, TWN = NW - TW0;
+    constexpr int MAXT = (L::NTILE + TWN - 1) / TWN;
+
     const int nchunks = (T + C - 1) / C;
-    if (nchunks > 0) prefetch(0);
+    // chunk 0 is staged before the loop; inside, chunk n+1 is loaded into
+    // registers at the top of iteration n and staged into LDS at its bottom,
+    // once chunk n is done with LDS.
+    float gcur = 1.f, bcur = 0.f;
+    if (nchunks > 0) {
+        prefetch(0);
+        stage(min(C, T), gcur, bcur);
+    }
 
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;
         const int cn = min(C, T - t0);
-        __syncthreads();                     // the previous chunk is done with LDS
-        stage();
         if (n + 1 < nchunks) prefetch(t0 + C);
-        __syncthreads();
+        lds_barrier();                     // chunk n staged
 
-        // ---- gates (wave 0): products of decays only
+        // ---- gates (wave 0, lane t holds g_t): products of decays only.
+        // P[t]: g over [block start, t]; Sfx[t]: over (t, block end];
+        // Rin[t][j']: over (block start + j', t]; block totals BT;
+        // G[t] = P[t] * BT of earlier blocks; Rl[t] = Sfx[t] * BT of later ones.
         if (wave == 0) {
-            const int t = lane;
-            const int bt = t >> 4, ti = t & 15, base = bt << 4;
-            float p = 1.f, s = 1.f;
-            if (t < C) {
+            const int t = lane, bt = t >> 4, ti = t & 15, base = bt << 4;
+            const float gt = (t < C) ? gcur : 1.f;
+            float gb[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float gi = sg[base + i];
-                    if (i <= ti) p *= gi;
-                    if (i > ti) s *= gi;
-                }
-                float r = 1.f;
+            for (int i = 0; i < 16; ++i) gb[i] = __shfl(gt, base + i);
+            float p = 1.f, sx = 1.f;
 #pragma unroll
-                for (int jj = 15; jj >= 0; --jj) {
-                    if (jj < ti) r *= sg[base + jj + 1];
-                    sRin[t * 16 + jj] = (jj <= ti) ? r : 0.f;
-                }
+            for (int i = 0; i < 16; ++i) {
+                if (i <= ti) p *= gb[i];
+                if (i > ti) sx *= gb[i];
             }
-            float bt_[NBT];
+            f32x4 rin[4];
+            float r = 1.f;
 #pragma unroll
-            for (int bb = 0; bb < NBT; ++bb) bt_[bb] = __shfl(p, 16 * bb + 15);
+            for (int jj = 15; jj >= 0; --jj) {
+                if (jj < ti) r *= gb[jj + 1];
+                rin[jj >> 2][jj & 3] = (jj <= ti) ? r : 0.f;
+            }
+            float btot[NBT];
+#pragma unroll
+            for (int bb = 0; bb < NBT; ++bb) btot[bb] = __shfl(p, 16 * bb + 15);
+            float gpre = p, rl = sx;
+#pragma unroll
+            for (int bb = 0; bb < NBT; ++bb) {
+                if (bb < bt) gpre *= btot[bb];
+                if (bb > bt) rl *= btot[bb];
+            }
             if (t < C) {
-                float gpre = p, rl = s;
-#pragma unroll
-                for (int bb = 0; bb < NBT; ++bb) {
-                    if (bb < bt) gpre *= bt_[bb];
-                    if (bb > bt) rl *= bt_[bb];
-                }
                 sP[t] = p;
-                sSfx[t] = s;
+                sSfx[t] = sx;
                 sG[t] = gpre;
                 sRl[t] = rl;
-                if (ti == 15) sBT[bt] = p;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    *reinterpret_cast<f32x4 *>(sRin + t * 16 + 4 * i4) = rin[i4];
+                if (t < NBT) sBT[t] = btot[t];
             }
         }
 
         // ---- K K^T and Q K^T lower block tiles, kept in registers.
         // Tile (jb, tb) has rows j (keys) and columns t, so lane x holds
         // row t = 16 tb + x of the result along j = 16 jb + 4 qd + r.
-        f32x4 tacc[L::MAXT];
+        f32x4 tacc[MAXT];
 #pragma unroll
-        for (int i = 0; i < L::MAXT; ++i) tacc[i] = zero4();
+        for (int i = 0; i < MAXT; ++i) tacc[i] = zero4();
         {
             int cnt = 0;
 #pragma unroll
@@ -351,7 +405,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 for (int tb = 0; tb < NBT; ++tb) {
 #pragma unroll
                     for (int jb = 0; jb <= tb; ++jb, ++cnt) {
-                        if (cnt % NW != wave) continue;
+                        if (TW0 + cnt % TWN != wave) continue;
                         const ET *bsrc = kind ? sQ : sK;
                         f32x4 acc = zero4();
 #pragma unroll
@@ -362,12 +416,39 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                                 return ld4<ET>(bsrc + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
                             acc = mfma_step(fa, fb, acc);
                         }
-                        tacc[cnt / NW] = acc;
+                        tacc[cnt / TWN] = acc;
                     }
                 }
             }
         }
-        __syncthreads();
+
+        // ---- state products that need no C x C matrix:
+        // X = K S0^T (tiles [t][v]) and Y^T = S0 Q^T (tiles [v][t])
+        X4 Sf[NBK][NB];
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) Sf[kb][vb] = cvt4<ET>(S[kb][vb]);
+        f32x4 Xa[NBT][NB], Ya[NB][NBT];
+#pragma unroll
+        for (int tb = 0; tb < NBT; ++tb) {
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) { Xa[tb][vb] = zero4(); Ya[vb][tb] = zero4(); }
+#pragma unroll
+            for (int s = 0; s < Steps<NBK, BLK>::n; ++s) {
+                FR fk = make_frag<ET>(s, NBK, [&](int kb) {
+                    return ld4<ET>(sK + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
+                FR fq = make_frag<ET>(s, NBK, [&](int kb) {
+                    return ld4<ET>(sQ + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    FR fs = make_frag<ET>(s, NBK, [&](int kb) { return Sf[kb][vb]; });
+                    Xa[tb][vb] = mfma_step(fk, fs, Xa[tb][vb]);
+                    Ya[vb][tb] = mfma_step(fs, fq, Ya[vb][tb]);
+                }
+            }
+        }
+        lds_barrier();
 
         // ---- A = beta R (K K^T) strictly lower; QKR = R (Q K^T) lower
         {
@@ -378,7 +459,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 for (int tb = 0; tb < NBT; ++tb) {
 #pragma unroll
                     for (int jb = 0; jb <= tb; ++jb, ++cnt) {
-                        if (cnt % NW != wave) continue;
+                        if (TW0 + cnt % TWN != wave) continue;
                         const int t = 16 * tb + x, j0 = 16 * jb + 4 * qd;
                         f32x4 R;
                         if (jb == tb) {
@@ -390,7 +471,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             const f32x4 sf = *reinterpret_cast<const f32x4 *>(sSfx + j0);
                             R = sf * m;
                         }
-                        const f32x4 z = tacc[cnt / NW];
+                        const f32x4 z = tacc[cnt / TWN];
                         f32x4 o;
                         if (kind == 0) {
                             const float bt = sb[t];
@@ -406,7 +487,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- T = (I + A)^-1: 16x16 diagonal blocks by forward substitution
         if (wave == 0 && lane < 16 * NBT) {
@@ -415,11 +496,15 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float *arow = sA + (base + i) * LDF + base;
+                f32x4 a4[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (4 * m < i) a4[m] = *reinterpret_cast<const f32x4 *>(arow + 4 * m);
                 float a0 = (i == c) ? 1.f : 0.f, a1 = 0.f;
 #pragma unroll
                 for (int j = 0; j < i; ++j) {
-                    if (j & 1) a1 -= arow[j] * xv[j];
-                    else a0 -= arow[j] * xv[j];
+                    if (j & 1) a1 -= a4[j >> 2][j & 3] * xv[j];
+                    else a0 -= a4[j >> 2][j & 3] * xv[j];
                 }
                 xv[i] = a0 + a1;
             }
@@ -430,7 +515,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
             for (int i = 0; i < 16; ++i) sT[(base + i) * LDF + base + c] = xv[i];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- first off-diagonal level: T[2p+1][2p] = -T[2p+1][2p+1] A[2p+1][2p] T[2p][2p]
         if constexpr (NBT >= 2) {
@@ -460,7 +545,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 for (int r = 0; r < 4; ++r) sT[(r0 + 16 + 4 * qd + r) * LDF + r0 + x] = X[r];
                 *reinterpret_cast<f32x4 *>(sTt + (r0 + x) * LDF + r0 + 16 + 4 * qd) = X;
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- second level (C = 64): T[32:64][0:32] = -T_b (A[32:64][0:32] T_a)
@@ -497,49 +582,29 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     *reinterpret_cast<f32x4 *>(sTt + (16 * jb + x) * LDF + 32 + 16 * ib + 4 * qd) = X;
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- T1 = T diag(beta), T2 = -T diag(beta G), as MFMA operands
-        for (int e = tid; e < C * C / 4; e += NT) {
-            const int t = e / (C / 4), c4 = (e - t * (C / 4)) * 4;
-            const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * LDF + c4);
-            const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + c4);
-            const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + c4);
-            const f32x4 t1 = tv * bv;
-            st4<ET>(sT1 + t * LDC + c4, cvt4<ET>(t1));
-            st4<ET>(sT2 + t * LDC + c4, cvt4<ET>(-(t1 * gv)));
-        }
-        __syncthreads();
-
-        // ---- state-dependent part, per wave over its value columns
-        X4 Sf[NBK][NB];
+        {
+            constexpr int ITEMS = C * C / 4, PER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-        for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-            for (int vb = 0; vb < NB; ++vb) Sf[kb][vb] = cvt4<ET>(S[kb][vb]);
-
-        // X = K S0^T  (tiles [t][v]);  Y^T = S0 Q^T  (tiles [v][t])
-        f32x4 Xa[NBT][NB], Ya[NB][NBT];
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-#pragma unroll
-            for (int vb = 0; vb < NB; ++vb) { Xa[tb][vb] = zero4(); Ya[vb][tb] = zero4(); }
-#pragma unroll
-            for (int s = 0; s < Steps<NBK, BLK>::n; ++s) {
-                FR fk = make_frag<ET>(s, NBK, [&](int kb) {
-                    return ld4<ET>(sK + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
-                FR fq = make_frag<ET>(s, NBK, [&](int kb) {
-                    return ld4<ET>(sQ + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    FR fs = make_frag<ET>(s, NBK, [&](int kb) { return Sf[kb][vb]; });
-                    Xa[tb][vb] = mfma_step(fk, fs, Xa[tb][vb]);
-                    Ya[vb][tb] = mfma_step(fs, fq, Ya[vb][tb]);
+            for (int i = 0; i < PER; ++i) {
+                const int e = tid + i * NT;
+                if (ITEMS % NT == 0 || e < ITEMS) {
+                    const int t = e / (C / 4), c4 = (e - t * (C / 4)) * 4;
+                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * LDF + c4);
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + c4);
+                    const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + c4);
+                    const f32x4 t1 = tv * bv;
+                    st4<ET>(sT1 + t * LDC + c4, cvt4<ET>(t1));
+                    st4<ET>(sT2 + t * LDC + c4, cvt4<ET>(-(t1 * gv)));
                 }
             }
         }
-        // G_t S0 q_t
+        lds_barrier();
+
+        // ---- G_t S0 q_t
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
             const float gt = sG[16 * tb + x];
@@ -631,6 +696,10 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     S[kb][vb] = mfma_step(fk, fd, S[kb][vb]);
                 }
             }
+        }
+        if (n + 1 < nchunks) {
+            lds_barrier();                 // chunk n is done with LDS
+            stage(min(C, T - t0 - C), gcur, bcur);
         }
     }
 

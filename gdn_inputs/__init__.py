@@ -63,16 +63,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
 
     NaN inputs map to a quiet NaN.  Written from the IEEE-754 definition of
-    the binary32 layout: bf16 keeps the upper 16 bits of the float32 word.
+    the binary32 layout: bf16 keeps the upper 16 bits of the float32 word;
+    adding 0x7FFF plus the lowest kept bit rounds the dropped half to nearest
+    even.  (The 32-bit sum cannot wrap for any non-NaN input.)
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        rounded = np.where(nan, np.uint16(0x7FC0), rounded)
-    return rounded
+        out[nan] = 0x7FC0
+    return out
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
