@@ -1,43 +1,44 @@
 // gdn_chunk_impl.h -- the chunked gated-delta-rule forward kernel for gfx950.
 //
-// One workgroup owns one (batch, value head) slot -- or a slice of its value
-// rows -- and walks the slot's T tokens in chunks of C, with the Dk x Dv
-// state resident in registers (as MFMA accumulator tiles of S^T) from the
-// first chunk to the last; the state is read from HBM once and written once.
+// One workgroup owns one (batch, value head) slot and walks its T tokens in
+// chunks of C, with the Dk x Dv state resident in registers (MFMA
+// accumulator tiles of S^T) from the first chunk to the last; the state is
+// read from HBM once and written once.
 //
 // Per chunk (c <= C tokens; rows past the end of the sequence are staged as
 // k = q = v = 0, g = 1, beta = 0, which leaves the recurrence unchanged --
 // the padding the metaltile-std gated_delta_wy.rs page asks its caller for):
 //
-//  stage    K, K^T, Q and this slice's V^T into LDS (16-bit or f32), g, beta.
-//  gates    chunk-local decay products, all formed by multiplying decays
-//           (ferrox-core gdn_chunk.rs page, "The algebra": ratios are
-//           products, an underflow is a state really forgotten):
-//             G[t]    = g_0 ... g_t,
-//             R[t][j] = g_{j+1} ... g_t  (j <= t),
-//           built from 16-token blocks: in-block rows by running products,
-//           across blocks as (prefix in t's block) x (whole blocks between)
-//           x (suffix in j's block).
-//  K K^T, Q K^T     (MFMA)  ->  A[t][j] = beta_t R[t][j] k_t.k_j  (j < t),
-//                               QKR[t][j] = R[t][j] q_t.k_j      (j <= t).
-//  T = (I + A)^-1   (f32 in LDS): 16x16 diagonal blocks by forward
-//           substitution, off-diagonal blocks by the block recurrence
-//           T_ij = -T_ii A_ij T_jj (two levels, MFMA).  This is the unit lower
-//           triangular system of the metaltile-std page's steps 4-5, solved
-//           once for every right-hand side of the chunk.
-//  X = K S0^T                          (MFMA, state-dependent)
-//  D = T diag(beta) V - T diag(beta G) X      -- the true per-token deltas
-//           d_t = beta_t (v_t - g_t S_{t-1} k_t) of all c tokens at once
-//           (ferrox-core page: the predictions written in S0 and the earlier
-//           deltas; one forward substitution for the whole chunk).
+//  stage    K, Q and this slice of V into LDS, row-major (transposed
+//           operands are read from the same rows with gfx950's LDS transpose
+//           load).
+//  gates    chunk-local decay products, every one formed by multiplying
+//           decays (ferrox-core gdn_chunk.rs page, "The algebra": a ratio is
+//           a product, and an underflow is a state really forgotten):
+//             G[t] = g_0 ... g_t,   R[t][j] = g_{j+1} ... g_t  (j <= t),
+//           from 16-token blocks: in-block rows by running products, across
+//           blocks (prefix in t's block) x (whole blocks between) x (suffix
+//           in j's block).
+//  X = K S0^T, Y^T = S0 Q^T and the C x C tiles K K^T, Q K^T (MFMA), all
+//           from one pass over the K and Q fragments;
+//           A[t][j] = beta_t R[t][j] k_t.k_j (j < t), QKR[t][j] = R[t][j] q_t.k_j (j <= t).
+//  T_ii = (I + A_ii)^-1 for the 16x16 diagonal blocks, f32 forward
+//           substitution (four lanes per column).
+//  D = (I + A)^-1 beta (V - G X): the true per-token deltas
+//           d_t = beta_t (v_t - g_t S_{t-1} k_t) of the whole chunk (the
+//           ferrox-core page's per-row forward substitution, written for all
+//           rows at once), by blocked forward substitution over 16-token
+//           blocks: D_i = T_ii (RHS_i - sum_{j<i} A_ij D_j)   (MFMA).
+//           This is the unit lower triangular system of the metaltile-std
+//           page's steps 4-5.
 //  y_t = (G_t S0 q_t + sum_{j<=t} R[t][j] (q_t.k_j) d_j) / sqrt(Dk)   (MFMA)
 //  S  <- G_{c-1} S0 + sum_t R[c-1][t] d_t k_t^T                        (MFMA)
 //
-// Work split: wave w of the workgroup owns 16*NB value columns of the
-// slice; it holds S^T[0:Dk, its columns] as NBK x NB accumulator tiles and
-// computes X, y and the update for its columns alone (each state row's
-// update needs only that row, k and the shared C x C matrices).  The C x C
-// work (gates, K K^T, Q K^T, T) is shared through LDS.
+// Work split: wave w owns 16*NB value columns of the slice and holds
+// S^T[0:Dk, its columns] as NBK x NB accumulator tiles; it computes X, D, y
+// and the update for its columns alone (a state row's update needs only that
+// row, k and the shared C x C matrices).  The C x C work is shared through
+// LDS; wave w computes the tile columns tb = w, w + NW, ...
 
 #pragma once
 
@@ -52,38 +53,36 @@ struct ChunkCfg {
     static constexpr int NT = 64 * NW;                // threads per workgroup
     static constexpr int NBT = C / 16;                // 16-token blocks per chunk
     static constexpr int NBK = DK / 16;               // 16-wide key blocks
-    static constexpr int EPU = 16 / (int)sizeof(ET);  // elements per 16-byte unit
-    static constexpr int LDK = DK + EPU;              // row stride of sK, sQ
-    static constexpr int LDC = C + 4;                 // row stride of sKt, sVt, sT1, sT2, sQKR
-                                                      // (odd multiple of 8 bytes / bank group)
-    static constexpr int LDF = C + 4;                 // row stride of f32 C x C matrices
+    static constexpr int NTPW = (NBT + NW - 1) / NW;  // tile columns per wave
     static constexpr int ES = (int)sizeof(ET);
+    static constexpr int EPU = 16 / ES;               // elements per 16-byte unit
+    // Row padding of 16 bytes: sixteen rows read at one column offset fall in
+    // sixteen different 4-bank groups.
+    static constexpr int LDK = DK + EPU;              // sK, sQ
+    static constexpr int LDV = DVS + EPU;             // sV
+    static constexpr int LDC = C + EPU;               // sAn, sQKR (16-bit rows of C)
+    static constexpr int LDR = C + 4;                 // sR (f32)
+    static constexpr int LDD = 16 + 4;                // sAd (f32 diagonal blocks)
+    static constexpr int LDT = 16 + EPU;              // sTd (diagonal inverses)
     static constexpr int oK = 0;
     static constexpr int oQ = oK + C * LDK * ES;
-    static constexpr int oKt = oQ + C * LDK * ES;
-    static constexpr int oVt = oKt + DK * LDC * ES;
-    static constexpr int oT1 = oVt + DVS * LDC * ES;  // T1..Tt: cleared once per launch
-    static constexpr int oT2 = oT1 + C * LDC * ES;
-    static constexpr int oQKR = oT2 + C * LDC * ES;
-    static constexpr int oA = oQKR + C * LDC * ES;
-    static constexpr int oT = oA + C * LDF * 4;
-    static constexpr int oTt = oT + C * LDF * 4;
-    static constexpr int oRin = oTt + C * LDF * 4;    // [C][16] in-block decay ratios
-    static constexpr int oVec = oRin + C * 16 * 4;    // g, beta, P, Sfx, G, Rlast, BT
-    static constexpr int BYTES = oVec + 8 * C * 4;
-    static constexpr int NPAIR = NBT * (NBT + 1) / 2;   // lower block tiles of C x C
-    static constexpr int NTILE = 2 * NPAIR;             // K K^T and Q K^T tiles
-    // staging: 16-byte units
-    static constexpr int UPK = DK / EPU;                // units per K / Q row
-    static constexpr int UPV = DVS / EPU;               // units per V row (slice)
-    static constexpr int KIT = (C / 4) * UPK;           // (4-row group, unit) items of K
-    static constexpr int QIT = C * UPK;
-    static constexpr int VIT = (C / 4) * UPV;
+    static constexpr int oV = oQ + C * LDK * ES;
+    static constexpr int oR = oV + C * LDV * ES;
+    static constexpr int oAn = oR + C * LDR * 4;
+    static constexpr int oQKR = oAn + C * LDC * ES;
+    static constexpr int oAd = oQKR + C * LDC * ES;
+    static constexpr int oTd = oAd + C * LDD * 4;
+    static constexpr int oVec = oTd + C * LDT * ES;   // beta, Sfx, G, Rlast
+    static constexpr int BYTES = oVec + 4 * C * 4;
+    // staging in 16-byte units
+    static constexpr int UPK = DK / EPU;
+    static constexpr int UPV = DVS / EPU;
+    static constexpr int KIT = C * UPK, VIT = C * UPV;
     static constexpr int PERK = (KIT + NT - 1) / NT;
-    static constexpr int PERQ = (QIT + NT - 1) / NT;
     static constexpr int PERV = (VIT + NT - 1) / NT;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(NW >= 1 && NW * 16 * NB == DVS, "value slice must split into whole waves");
+    static_assert(LDK % 4 == 0 && LDV % 4 == 0, "transpose loads need 8-byte aligned rows");
 };
 
 // A fragment over one contraction step: two 16-blocks (16-bit types, one
@@ -96,6 +95,8 @@ template <> struct Step<float> {
     static constexpr int BLK = 1;
     using frag = f32x4;
 };
+
+template <int NBLK, int BLK> struct Steps { static constexpr int n = (NBLK + BLK - 1) / BLK; };
 
 // Fragment of contraction step s from per-block fetches fb(kb); blocks at or
 // past `lim` read as zero.
@@ -122,19 +123,49 @@ __device__ __forceinline__ f32x4 mfma_step(f32x4 a, f32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_step(bf16x8 a, bf16x8 b, f32x4 c) { return mfma(a, b, c); }
 __device__ __forceinline__ f32x4 mfma_step(f16x8 a, f16x8 b, f32x4 c) { return mfma(a, b, c); }
 
-template <int NBLK, int BLK> struct Steps { static constexpr int n = (NBLK + BLK - 1) / BLK; };
+// Row fragment of a row-major matrix: lane (x, qd) holds row r0 + x,
+// columns c0 + 16 kb + 4 qd + (0..3).
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x4 frag_row(const ET *m, int ld, int r0, int c0, int kb, int x, int qd) {
+    return ld4<ET>(m + (r0 + x) * ld + c0 + 16 * kb + 4 * qd);
+}
 
-template <typename ET> union Unit16 {
-    uint4 u;
-    ET e[16 / sizeof(ET)];
-};
+// Column fragment of a row-major matrix (the fragment of its transpose):
+// lane (x, qd) holds column c0 + x, rows r0 + 16 kb + 4 qd + (0..3).  For
+// 16-bit types one LDS transpose load does it: within each group of 16
+// lanes, lane m receives element m%4 of the 8-byte pieces addressed by lanes
+// m/4 + 4i (i = 0..3), so lane j points at row j/4, columns 4 (j%4) .. +3.
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x4 frag_col(const ET *m, int ld, int r0, int c0, int kb, int x, int qd) {
+    const int rb = r0 + 16 * kb + 4 * qd;
+    if constexpr (sizeof(ET) == 2) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const ET *p = m + (rb + (x >> 2)) * ld + c0 + 4 * (x & 3);
+        const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(p));
+        return __builtin_bit_cast(typename Vec<ET>::x4, raw);
+    } else {
+        typename Vec<ET>::x4 r;
+        r[0] = m[(rb + 0) * ld + c0 + x];
+        r[1] = m[(rb + 1) * ld + c0 + x];
+        r[2] = m[(rb + 2) * ld + c0 + x];
+        r[3] = m[(rb + 3) * ld + c0 + x];
+        return r;
+    }
+}
+
+// Broadcast lane K of every group of four lanes to the group (DPP quad_perm).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xf, 0xf, false));
+}
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, then for every wave.  Unlike __syncthreads() it does not wait
-// for outstanding global loads and stores, so the next chunk's prefetch and
-// this chunk's y stores stay in flight across it.
+// for outstanding global loads and stores, so the next chunk's loads and this
+// chunk's y stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -151,28 +182,25 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     using X4 = typename Vec<ET>::x4;
     using FR = typename Step<ET>::frag;
     constexpr int BLK = Step<ET>::BLK;
-    constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT;
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, EPU = L::EPU;
+    constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT, NTPW = L::NTPW;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDR = L::LDR, LDD = L::LDD,
+                  LDT = L::LDT, EPU = L::EPU;
+    constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
+    constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     ET *sK = reinterpret_cast<ET *>(smem + L::oK);
     ET *sQ = reinterpret_cast<ET *>(smem + L::oQ);
-    ET *sKt = reinterpret_cast<ET *>(smem + L::oKt);
-    ET *sVt = reinterpret_cast<ET *>(smem + L::oVt);
-    ET *sT1 = reinterpret_cast<ET *>(smem + L::oT1);
-    ET *sT2 = reinterpret_cast<ET *>(smem + L::oT2);
+    ET *sV = reinterpret_cast<ET *>(smem + L::oV);
+    float *sR = reinterpret_cast<float *>(smem + L::oR);
+    ET *sAn = reinterpret_cast<ET *>(smem + L::oAn);    // -A (16-bit)
     ET *sQKR = reinterpret_cast<ET *>(smem + L::oQKR);
-    float *sA = reinterpret_cast<float *>(smem + L::oA);
-    float *sT = reinterpret_cast<float *>(smem + L::oT);
-    float *sTt = reinterpret_cast<float *>(smem + L::oTt);
-    float *sRin = reinterpret_cast<float *>(smem + L::oRin);
-    float *sg = reinterpret_cast<float *>(smem + L::oVec);
-    float *sb = sg + C;
-    float *sP = sb + C;
-    float *sSfx = sP + C;
+    float *sAd = reinterpret_cast<float *>(smem + L::oAd);  // diagonal blocks of A (f32)
+    ET *sTd = reinterpret_cast<ET *>(smem + L::oTd);    // diagonal blocks of (I + A)^-1
+    float *sb = reinterpret_cast<float *>(smem + L::oVec);
+    float *sSfx = sb + C;
     float *sG = sSfx + C;
     float *sRl = sG + C;
-    float *sBT = sRl + C;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, x = lane & 15, qd = lane >> 4;
@@ -209,14 +237,9 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
         for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
 
-    // ---- structural zeros of the C x C matrices (upper triangles never written)
-    for (int i = tid; i < (L::oRin - L::oT1) / 16; i += NT)
-        reinterpret_cast<uint4 *>(smem + L::oT1)[i] = zero_u4();
-
     // ---- global -> register prefetch of one chunk.  Every load is issued
     // unconditionally from a clamped (always valid) row; rows past the end
-    // of the sequence are zeroed when the registers are staged, so nothing
-    // consumes the loaded values before the next chunk's staging point.
+    // of the sequence are zeroed when the registers are staged.
     const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * Dv;
     const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
     const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
@@ -224,84 +247,47 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const float *gbase = g + (size_t)b * T * Hv + hv;
     const float *bbase = beta + (size_t)b * T * Hv + hv;
 
-    uint4 rk[L::PERK][4], rq[L::PERQ], rv[L::PERV][4];
+    uint4 rk[L::PERK], rq[L::PERK], rv[L::PERV];
     float rg = 1.f, rb = 0.f;
     auto prefetch = [&](int t0) {
         const int last = min(C, T - t0) - 1;
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
             const int it = min(tid + i * NT, L::KIT - 1);
-            const int rgp = it / L::UPK, u = it - rgp * L::UPK;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = min(4 * rgp + r, last);
-                rk[i][r] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(t0 + t) * kstride + u * EPU);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < L::PERQ; ++i) {
-            const int it = min(tid + i * NT, L::QIT - 1);
             const int t = min(it / L::UPK, last), u = it % L::UPK;
+            rk[i] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(t0 + t) * kstride + u * EPU);
             rq[i] = *reinterpret_cast<const uint4 *>(qbase + (size_t)(t0 + t) * kstride + u * EPU);
         }
 #pragma unroll
         for (int i = 0; i < L::PERV; ++i) {
             const int it = min(tid + i * NT, L::VIT - 1);
-            const int rgp = it / L::UPV, u = it - rgp * L::UPV;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = min(4 * rgp + r, last);
-                rv[i][r] = *reinterpret_cast<const uint4 *>(vbase + (size_t)(t0 + t) * vstride + u * EPU);
-            }
+            const int t = min(it / L::UPV, last), u = it % L::UPV;
+            rv[i] = *reinterpret_cast<const uint4 *>(vbase + (size_t)(t0 + t) * vstride + u * EPU);
         }
         const int tg = min(tid, last);
         rg = gbase[(size_t)(t0 + tg) * Hv];
         rb = bbase[(size_t)(t0 + tg) * Hv];
     };
 
-    // Registers -> LDS: K row-major and transposed, Q, the V slice
-    // transposed, g and beta; rows t >= cn become k = q = v = 0, g = 1,
-    // beta = 0.  The empty asm statements pin the point where the prefetched
-    // values are first needed here, after the barrier.
-    auto stage = [&](int cn, float &gcur, float &bcur) {
+    // Registers -> LDS (row-major K, Q, V; beta); rows t >= cn become zero,
+    // g = 1, beta = 0.  The empty asm statements pin the point where the
+    // prefetched values are first needed here, after the barrier.
+    auto stage = [&](int cn, float &gcur) {
 #pragma unroll
-        for (int i = 0; i < L::PERK; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                asm volatile("" : "+v"(rk[i][r].x), "+v"(rk[i][r].y), "+v"(rk[i][r].z), "+v"(rk[i][r].w));
-#pragma unroll
-        for (int i = 0; i < L::PERQ; ++i)
+        for (int i = 0; i < L::PERK; ++i) {
+            asm volatile("" : "+v"(rk[i].x), "+v"(rk[i].y), "+v"(rk[i].z), "+v"(rk[i].w));
             asm volatile("" : "+v"(rq[i].x), "+v"(rq[i].y), "+v"(rq[i].z), "+v"(rq[i].w));
+        }
 #pragma unroll
         for (int i = 0; i < L::PERV; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                asm volatile("" : "+v"(rv[i][r].x), "+v"(rv[i][r].y), "+v"(rv[i][r].z), "+v"(rv[i][r].w));
+            asm volatile("" : "+v"(rv[i].x), "+v"(rv[i].y), "+v"(rv[i].z), "+v"(rv[i].w));
         asm volatile("" : "+v"(rg), "+v"(rb));
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
             const int it = tid + i * NT;
             if (L::KIT % NT == 0 || it < L::KIT) {
-                const int rgp = it / L::UPK, u = it - rgp * L::UPK;
-                Unit16<ET> w[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    w[r].u = (4 * rgp + r < cn) ? rk[i][r] : zero_u4();
-                    *reinterpret_cast<uint4 *>(sK + (4 * rgp + r) * LDK + u * EPU) = w[r].u;
-                }
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) {
-                    X4 col;
-                    col[0] = w[0].e[e]; col[1] = w[1].e[e]; col[2] = w[2].e[e]; col[3] = w[3].e[e];
-                    st4<ET>(sKt + (u * EPU + e) * LDC + 4 * rgp, col);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < L::PERQ; ++i) {
-            const int it = tid + i * NT;
-            if (L::QIT % NT == 0 || it < L::QIT) {
                 const int t = it / L::UPK, u = it - t * L::UPK;
+                *reinterpret_cast<uint4 *>(sK + t * LDK + u * EPU) = (t < cn) ? rk[i] : zero_u4();
                 *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = (t < cn) ? rq[i] : zero_u4();
             }
         }
@@ -309,36 +295,22 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         for (int i = 0; i < L::PERV; ++i) {
             const int it = tid + i * NT;
             if (L::VIT % NT == 0 || it < L::VIT) {
-                const int rgp = it / L::UPV, u = it - rgp * L::UPV;
-                Unit16<ET> w[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) w[r].u = (4 * rgp + r < cn) ? rv[i][r] : zero_u4();
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) {
-                    X4 col;
-                    col[0] = w[0].e[e]; col[1] = w[1].e[e]; col[2] = w[2].e[e]; col[3] = w[3].e[e];
-                    st4<ET>(sVt + (u * EPU + e) * LDC + 4 * rgp, col);
-                }
+                const int t = it / L::UPV, u = it - t * L::UPV;
+                *reinterpret_cast<uint4 *>(sV + t * LDV + u * EPU) = (t < cn) ? rv[i] : zero_u4();
             }
         }
         gcur = (tid < cn) ? rg : 1.f;
-        bcur = (tid < cn) ? rb : 0.f;
-        if (tid < C) sb[tid] = bcur;
+        if (tid < C) sb[tid] = (tid < cn) ? rb : 0.f;
     };
-
-    // Which wave computes shared K K^T / Q K^T tile number cnt: with four or
-    // more waves, wave 0 (which also forms the gate products) is skipped.
-    constexpr int TW0 = NW >= 4 ? 1 : 0, TWN = NW - TW0;
-    constexpr int MAXT = (L::NTILE + TWN - 1) / TWN;
 
     const int nchunks = (T + C - 1) / C;
     // chunk 0 is staged before the loop; inside, chunk n+1 is loaded into
     // registers at the top of iteration n and staged into LDS at its bottom,
     // once chunk n is done with LDS.
-    float gcur = 1.f, bcur = 0.f;
+    float gcur = 1.f;
     if (nchunks > 0) {
         prefetch(0);
-        stage(min(C, T), gcur, bcur);
+        stage(min(C, T), gcur);
     }
 
     for (int n = 0; n < nchunks; ++n) {
@@ -349,8 +321,9 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 
         // ---- gates (wave 0, lane t holds g_t): products of decays only.
         // P[t]: g over [block start, t]; Sfx[t]: over (t, block end];
-        // Rin[t][j']: over (block start + j', t]; block totals BT;
-        // G[t] = P[t] * BT of earlier blocks; Rl[t] = Sfx[t] * BT of later ones.
+        // in-block ratios over (block start + j', t]; block totals BT;
+        // G[t] = P[t] * BT of earlier blocks; Rl[t] = Sfx[t] * BT of later
+        // ones; R[t][j] for an earlier block = P[t] * BT between * Sfx[j].
         if (wave == 0) {
             const int t = lane, bt = t >> 4, ti = t & 15, base = bt << 4;
             const float gt = (t < C) ? gcur : 1.f;
@@ -363,6 +336,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 if (i <= ti) p *= gb[i];
                 if (i > ti) sx *= gb[i];
             }
+            if (t < C) sSfx[t] = sx;
             f32x4 rin[4];
             float r = 1.f;
 #pragma unroll
@@ -380,289 +354,209 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 if (bb > bt) rl *= btot[bb];
             }
             if (t < C) {
-                sP[t] = p;
-                sSfx[t] = sx;
                 sG[t] = gpre;
                 sRl[t] = rl;
+                // row t of R: blocks before t's own (products through the
+                // whole blocks in between), t's own block, zeros after
+                float m = p;                 // P[t] * BT(bt-1) * ... going left
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4)
-                    *reinterpret_cast<f32x4 *>(sRin + t * 16 + 4 * i4) = rin[i4];
-                if (t < NBT) sBT[t] = btot[t];
-            }
-        }
-
-        // ---- K K^T and Q K^T lower block tiles, kept in registers.
-        // Tile (jb, tb) has rows j (keys) and columns t, so lane x holds
-        // row t = 16 tb + x of the result along j = 16 jb + 4 qd + r.
-        f32x4 tacc[MAXT];
+                for (int jb = NBT - 1; jb >= 0; --jb) {
+                    f32x4 o[4];
+                    if (jb == bt) {
 #pragma unroll
-        for (int i = 0; i < MAXT; ++i) tacc[i] = zero4();
-        {
-            int cnt = 0;
+                        for (int i4 = 0; i4 < 4; ++i4) o[i4] = rin[i4];
+                    } else if (jb < bt) {
 #pragma unroll
-            for (int kind = 0; kind < 2; ++kind) {
+                        for (int i4 = 0; i4 < 4; ++i4)
+                            o[i4] = *reinterpret_cast<const f32x4 *>(sSfx + 16 * jb + 4 * i4) * m;
+                    } else {
 #pragma unroll
-                for (int tb = 0; tb < NBT; ++tb) {
-#pragma unroll
-                    for (int jb = 0; jb <= tb; ++jb, ++cnt) {
-                        if (TW0 + cnt % TWN != wave) continue;
-                        const ET *bsrc = kind ? sQ : sK;
-                        f32x4 acc = zero4();
-#pragma unroll
-                        for (int s = 0; s < Steps<NBK, BLK>::n; ++s) {
-                            FR fa = make_frag<ET>(s, NBK, [&](int kb) {
-                                return ld4<ET>(sK + (16 * jb + x) * LDK + 16 * kb + 4 * qd); });
-                            FR fb = make_frag<ET>(s, NBK, [&](int kb) {
-                                return ld4<ET>(bsrc + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
-                            acc = mfma_step(fa, fb, acc);
-                        }
-                        tacc[cnt / TWN] = acc;
+                        for (int i4 = 0; i4 < 4; ++i4) o[i4] = zero4();
                     }
+                    if (jb < bt) m *= btot[jb];
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        *reinterpret_cast<f32x4 *>(sR + t * LDR + 16 * jb + 4 * i4) = o[i4];
                 }
             }
         }
 
-        // ---- state products that need no C x C matrix:
-        // X = K S0^T (tiles [t][v]) and Y^T = S0 Q^T (tiles [v][t])
+        // ---- one pass over the K and Q fragments:
+        //   X = K S0^T (tiles [t][v]), Y^T = S0 Q^T (tiles [v][t]) for this
+        //   wave's columns, and the C x C tile columns tb = wave + i*NW of
+        //   K K^T and Q K^T: tile (jb, tb) has rows j and columns t, so lane
+        //   x holds row t = 16 tb + x along j = 16 jb + 4 qd + r.
         X4 Sf[NBK][NB];
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) Sf[kb][vb] = cvt4<ET>(S[kb][vb]);
         f32x4 Xa[NBT][NB], Ya[NB][NBT];
+        f32x4 tkk[NTPW][NBT], tqk[NTPW][NBT];
 #pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
+        for (int tb = 0; tb < NBT; ++tb)
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) { Xa[tb][vb] = zero4(); Ya[vb][tb] = zero4(); }
 #pragma unroll
-            for (int s = 0; s < Steps<NBK, BLK>::n; ++s) {
-                FR fk = make_frag<ET>(s, NBK, [&](int kb) {
-                    return ld4<ET>(sK + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
-                FR fq = make_frag<ET>(s, NBK, [&](int kb) {
-                    return ld4<ET>(sQ + (16 * tb + x) * LDK + 16 * kb + 4 * qd); });
+        for (int i = 0; i < NTPW; ++i)
 #pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    FR fs = make_frag<ET>(s, NBK, [&](int kb) { return Sf[kb][vb]; });
-                    Xa[tb][vb] = mfma_step(fk, fs, Xa[tb][vb]);
-                    Ya[vb][tb] = mfma_step(fs, fq, Ya[vb][tb]);
-                }
+            for (int jb = 0; jb < NBT; ++jb) { tkk[i][jb] = zero4(); tqk[i][jb] = zero4(); }
+#pragma unroll
+        for (int s = 0; s < NSK; ++s) {
+            FR fk[NBT], fq[NBT];
+#pragma unroll
+            for (int tb = 0; tb < NBT; ++tb) {
+                fk[tb] = make_frag<ET>(s, NBK, [&](int kb) { return frag_row<ET>(sK, LDK, 16 * tb, 0, kb, x, qd); });
+                fq[tb] = make_frag<ET>(s, NBK, [&](int kb) { return frag_row<ET>(sQ, LDK, 16 * tb, 0, kb, x, qd); });
             }
-        }
-        lds_barrier();
-
-        // ---- A = beta R (K K^T) strictly lower; QKR = R (Q K^T) lower
-        {
-            int cnt = 0;
 #pragma unroll
-            for (int kind = 0; kind < 2; ++kind) {
+            for (int vb = 0; vb < NB; ++vb) {
+                FR fs = make_frag<ET>(s, NBK, [&](int kb) { return Sf[kb][vb]; });
 #pragma unroll
                 for (int tb = 0; tb < NBT; ++tb) {
+                    Xa[tb][vb] = mfma_step(fk[tb], fs, Xa[tb][vb]);
+                    Ya[vb][tb] = mfma_step(fs, fq[tb], Ya[vb][tb]);
+                }
+            }
 #pragma unroll
-                    for (int jb = 0; jb <= tb; ++jb, ++cnt) {
-                        if (TW0 + cnt % TWN != wave) continue;
-                        const int t = 16 * tb + x, j0 = 16 * jb + 4 * qd;
-                        f32x4 R;
-                        if (jb == tb) {
-                            R = *reinterpret_cast<const f32x4 *>(sRin + t * 16 + 4 * qd);
-                        } else {
-                            float m = sP[t];
+            for (int i = 0; i < NTPW; ++i) {
+                const int tbw = wave + i * NW;             // this wave's tile column
+                FR bk = fk[0], bq = fq[0];
 #pragma unroll
-                            for (int bb = jb + 1; bb < tb; ++bb) m *= sBT[bb];
-                            const f32x4 sf = *reinterpret_cast<const f32x4 *>(sSfx + j0);
-                            R = sf * m;
-                        }
-                        const f32x4 z = tacc[cnt / TWN];
-                        f32x4 o;
-                        if (kind == 0) {
-                            const float bt = sb[t];
+                for (int tb = 1; tb < NBT; ++tb)
+                    if (tb == tbw) { bk = fk[tb]; bq = fq[tb]; }
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) o[r] = (j0 + r < t) ? bt * (R[r] * z[r]) : 0.f;
-                            *reinterpret_cast<f32x4 *>(sA + t * LDF + j0) = o;
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) o[r] = (j0 + r <= t) ? R[r] * z[r] : 0.f;
-                            st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
-                        }
-                    }
+                for (int jb = 0; jb < NBT; ++jb) {
+                    tkk[i][jb] = mfma_step(fk[jb], bk, tkk[i][jb]);
+                    tqk[i][jb] = mfma_step(fk[jb], bq, tqk[i][jb]);
                 }
             }
         }
         lds_barrier();
 
-        // ---- T = (I + A)^-1: 16x16 diagonal blocks by forward substitution
-        if (wave == 0 && lane < 16 * NBT) {
-            const int bb = lane >> 4, c = lane & 15, base = 16 * bb;
-            float xv[16];
+        // ---- A = beta R (K K^T) strictly lower (as -A, 16-bit, and its
+        // diagonal blocks in f32); QKR = R (Q K^T) lower, incl. the diagonal
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float *arow = sA + (base + i) * LDF + base;
-                f32x4 a4[4];
+        for (int i = 0; i < NTPW; ++i) {
+            const int tb = wave + i * NW;
+            if (NBT % NW == 0 || tb < NBT) {
+                const int t = 16 * tb + x;
+                const float bt = sb[t];
+#pragma unroll
+                for (int jb = 0; jb < NBT; ++jb) {
+                    const int j0 = 16 * jb + 4 * qd;
+                    const f32x4 R = *reinterpret_cast<const f32x4 *>(sR + t * LDR + j0);
+                    const f32x4 zk = tkk[i][jb], zq = tqk[i][jb];
+                    f32x4 a, o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        a[r] = (j0 + r < t) ? bt * (R[r] * zk[r]) : 0.f;
+                        o[r] = (j0 + r <= t) ? R[r] * zq[r] : 0.f;
+                    }
+                    st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
+                    st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
+                    if (jb == tb) *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- T_bb = (I + A_bb)^-1 for the 16x16 diagonal blocks: wave w
+        // solves blocks w, w + NW, ...; four lanes per column c, lane part p
+        // holding rows p, p+4, p+8, p+12.  Column sweep: once x_j is final
+        // (it sits in part j%4), every later row subtracts A[i][j] x_j.
+#pragma unroll
+        for (int i = 0; i < NTPW; ++i) {
+            const int bb = wave + i * NW;
+            if (NBT % NW == 0 || bb < NBT) {
+                const int base = 16 * bb;
+                const int p = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
+                f32x4 arow[4][4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    if (4 * m < i) a4[m] = *reinterpret_cast<const f32x4 *>(arow + 4 * m);
-                float a0 = (i == c) ? 1.f : 0.f, a1 = 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) {
-                    if (j & 1) a1 -= a4[j >> 2][j & 3] * xv[j];
-                    else a0 -= a4[j >> 2][j & 3] * xv[j];
-                }
-                xv[i] = a0 + a1;
-            }
+                    for (int j4 = 0; j4 < 4; ++j4)
+                        arow[m][j4] = *reinterpret_cast<const f32x4 *>(sAd + (base + p + 4 * m) * LDD + 4 * j4);
+                float s[4];
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                *reinterpret_cast<f32x4 *>(sTt + (base + c) * LDF + base + 4 * i4) =
-                    f32x4{xv[4 * i4], xv[4 * i4 + 1], xv[4 * i4 + 2], xv[4 * i4 + 3]};
+                for (int m = 0; m < 4; ++m) s[m] = (p + 4 * m == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(base + i) * LDF + base + c] = xv[i];
-        }
-        lds_barrier();
-
-        // ---- first off-diagonal level: T[2p+1][2p] = -T[2p+1][2p+1] A[2p+1][2p] T[2p][2p]
-        if constexpr (NBT >= 2) {
-#pragma unroll
-            for (int p = 0; p < NBT / 2; ++p) {
-                if (p % NW != wave) continue;
-                const int r0 = 32 * p;
-                f32x4 P = zero4();
-#pragma unroll
-                for (int s = 0; s < Steps<1, BLK>::n; ++s) {
-                    FR fa = make_frag<ET>(s, 1, [&](int) {
-                        return cvt4<ET>(*reinterpret_cast<const f32x4 *>(sA + (r0 + 16 + x) * LDF + r0 + 4 * qd)); });
-                    FR fb = make_frag<ET>(s, 1, [&](int) {
-                        return cvt4<ET>(*reinterpret_cast<const f32x4 *>(sTt + (r0 + x) * LDF + r0 + 4 * qd)); });
-                    P = mfma_step(fa, fb, P);
-                }
-                const X4 Pf = cvt4<ET>(P);
-                f32x4 X = zero4();
-#pragma unroll
-                for (int s = 0; s < Steps<1, BLK>::n; ++s) {
-                    FR fa = make_frag<ET>(s, 1, [&](int) {
-                        return cvt4<ET>(-*reinterpret_cast<const f32x4 *>(sT + (r0 + 16 + x) * LDF + r0 + 16 + 4 * qd)); });
-                    FR fb = make_frag<ET>(s, 1, [&](int) { return Pf; });
-                    X = mfma_step(fa, fb, X);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sT[(r0 + 16 + 4 * qd + r) * LDF + r0 + x] = X[r];
-                *reinterpret_cast<f32x4 *>(sTt + (r0 + x) * LDF + r0 + 16 + 4 * qd) = X;
-            }
-            lds_barrier();
-        }
-
-        // ---- second level (C = 64): T[32:64][0:32] = -T_b (A[32:64][0:32] T_a)
-        if constexpr (NBT == 4) {
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                if (jb % NW != wave) continue;
-                X4 Pf[2];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    f32x4 P = zero4();
-#pragma unroll
-                    for (int s = 0; s < Steps<2, BLK>::n; ++s) {
-                        FR fa = make_frag<ET>(s, 2, [&](int kb) {
-                            return cvt4<ET>(*reinterpret_cast<const f32x4 *>(sA + (32 + 16 * ib + x) * LDF + 16 * kb + 4 * qd)); });
-                        FR fb = make_frag<ET>(s, 2, [&](int kb) {
-                            return cvt4<ET>(*reinterpret_cast<const f32x4 *>(sTt + (16 * jb + x) * LDF + 16 * kb + 4 * qd)); });
-                        P = mfma_step(fa, fb, P);
-                    }
-                    Pf[ib] = cvt4<ET>(P);
-                }
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    f32x4 X = zero4();
-#pragma unroll
-                    for (int s = 0; s < Steps<2, BLK>::n; ++s) {
-                        FR fa = make_frag<ET>(s, 2, [&](int kb) {
-                            return cvt4<ET>(-*reinterpret_cast<const f32x4 *>(sT + (32 + 16 * ib + x) * LDF + 32 + 16 * kb + 4 * qd)); });
-                        FR fb = make_frag<ET>(s, 2, [&](int kb) { return Pf[kb]; });
-                        X = mfma_step(fa, fb, X);
+                for (int j = 0; j < 15; ++j) {
+                    float xj;
+                    switch (j & 3) {
+                    case 0: xj = quad_bcast<0>(s[j >> 2]); break;
+                    case 1: xj = quad_bcast<1>(s[j >> 2]); break;
+                    case 2: xj = quad_bcast<2>(s[j >> 2]); break;
+                    default: xj = quad_bcast<3>(s[j >> 2]); break;
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sT[(32 + 16 * ib + 4 * qd + r) * LDF + 16 * jb + x] = X[r];
-                    *reinterpret_cast<f32x4 *>(sTt + (16 * jb + x) * LDF + 32 + 16 * ib + 4 * qd) = X;
+                    for (int m = 0; m < 4; ++m)
+                        if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;   // A[i][j] = 0 for j >= i
                 }
-            }
-            lds_barrier();
-        }
-
-        // ---- T1 = T diag(beta), T2 = -T diag(beta G), as MFMA operands
-        {
-            constexpr int ITEMS = C * C / 4, PER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int e = tid + i * NT;
-                if (ITEMS % NT == 0 || e < ITEMS) {
-                    const int t = e / (C / 4), c4 = (e - t * (C / 4)) * 4;
-                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * LDF + c4);
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + c4);
-                    const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + c4);
-                    const f32x4 t1 = tv * bv;
-                    st4<ET>(sT1 + t * LDC + c4, cvt4<ET>(t1));
-                    st4<ET>(sT2 + t * LDC + c4, cvt4<ET>(-(t1 * gv)));
-                }
+                for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
             }
         }
         lds_barrier();
 
-        // ---- G_t S0 q_t
+        // ---- D by blocked forward substitution (per wave, its columns):
+        // RHS = beta (V - G X); D_i = T_ii (RHS_i + sum_{j<i} (-A_ij) D_j).
+        // Fragments over rows t: lane x holds column v, rows 16 i + 4 qd + r.
+        f32x4 Da[NBT][NB];
+        X4 Df[NBT][NB];
+#pragma unroll
+        for (int ib = 0; ib < NBT; ++ib) {
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + 16 * ib + 4 * qd);
+            const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + 16 * ib + 4 * qd);
+            f32x4 Z[NB];
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) {
+                const f32x4 vv = to_f32x4<ET>(frag_col<ET>(sV, LDV, 0, vloc + 16 * vb, ib, x, qd));
+                Z[vb] = bv * (vv - gv * Xa[ib][vb]);
+            }
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+                if (s * BLK >= ib) continue;              // blocks j < ib only
+                FR fa = make_frag<ET>(s, ib, [&](int jb) { return frag_row<ET>(sAn, LDC, 16 * ib, 0, jb, x, qd); });
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    FR fd = make_frag<ET>(s, ib, [&](int jb) { return Df[jb][vb]; });
+                    Z[vb] = mfma_step(fa, fd, Z[vb]);
+                }
+            }
+            FR ft = make_frag<ET>(0, 1, [&](int) { return frag_row<ET>(sTd, LDT, 16 * ib, 0, 0, x, qd); });
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) {
+                FR fz = make_frag<ET>(0, 1, [&](int) { return cvt4<ET>(Z[vb]); });
+                Da[ib][vb] = mfma_step(ft, fz, zero4());
+                Df[ib][vb] = cvt4<ET>(Da[ib][vb]);
+            }
+        }
+
+        // ---- Y^T = G (S0 Q^T) + D^T QKR^T  (intra-chunk term)
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
             const float gt = sG[16 * tb + x];
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) Ya[vb][tb] *= gt;
-        }
-
-        // D = T1 V + T2 X  (T2 holds -T diag(beta G))
-        X4 Xf[NBT][NB];
+            FR fr[NST];
 #pragma unroll
-        for (int tb = 0; tb < NBT; ++tb)
-#pragma unroll
-            for (int vb = 0; vb < NB; ++vb) Xf[tb][vb] = cvt4<ET>(Xa[tb][vb]);
-        f32x4 Da[NBT][NB];
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-#pragma unroll
-            for (int vb = 0; vb < NB; ++vb) Da[tb][vb] = zero4();
-#pragma unroll
-            for (int s = 0; s < Steps<NBT, BLK>::n; ++s) {
-                if (s * BLK > tb) continue;          // T is lower triangular
-                FR f1 = make_frag<ET>(s, NBT, [&](int jb) {
-                    return ld4<ET>(sT1 + (16 * tb + x) * LDC + 16 * jb + 4 * qd); });
-                FR f2 = make_frag<ET>(s, NBT, [&](int jb) {
-                    return ld4<ET>(sT2 + (16 * tb + x) * LDC + 16 * jb + 4 * qd); });
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    FR fv = make_frag<ET>(s, NBT, [&](int jb) {
-                        return ld4<ET>(sVt + (vloc + 16 * vb + x) * LDC + 16 * jb + 4 * qd); });
-                    FR fx = make_frag<ET>(s, NBT, [&](int jb) { return Xf[jb][vb]; });
-                    Da[tb][vb] = mfma_step(f1, fv, Da[tb][vb]);
-                    Da[tb][vb] = mfma_step(f2, fx, Da[tb][vb]);
-                }
-            }
-        }
-
-        // Y^T += D^T QKR^T  (intra-chunk term)
-        X4 Df[NBT][NB];
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb)
-#pragma unroll
-            for (int vb = 0; vb < NB; ++vb) Df[tb][vb] = cvt4<ET>(Da[tb][vb]);
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-#pragma unroll
-            for (int s = 0; s < Steps<NBT, BLK>::n; ++s) {
+            for (int s = 0; s < NST; ++s) {
                 if (s * BLK > tb) continue;
-                FR fr = make_frag<ET>(s, NBT, [&](int jb) {
-                    return ld4<ET>(sQKR + (16 * tb + x) * LDC + 16 * jb + 4 * qd); });
+                fr[s] = make_frag<ET>(s, NBT, [&](int jb) { return frag_row<ET>(sQKR, LDC, 16 * tb, 0, jb, x, qd); });
+            }
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+                if (s * BLK > tb) continue;
 #pragma unroll
                 for (int vb = 0; vb < NB; ++vb) {
                     FR fd = make_frag<ET>(s, NBT, [&](int jb) { return Df[jb][vb]; });
-                    Ya[vb][tb] = mfma_step(fd, fr, Ya[vb][tb]);
+                    Ya[vb][tb] = mfma_step(fd, fr[s], Ya[vb][tb]);
                 }
             }
         }
 
-        // y store: lane holds token t = 16 tb + x, values 16 vb + 4 qd + (0..3)
+        // ---- y store: lane holds token t = 16 tb + x, values 16 vb + 4 qd + (0..3)
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
             const int t = 16 * tb + x;
@@ -673,7 +567,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
         }
 
-        // S^T <- G_last S^T + K^T diag(R[c-1][:]) D
+        // ---- S^T <- G_last S^T + K^T diag(R[c-1][:]) D
         X4 Dpf[NBT][NB];
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
@@ -684,22 +578,24 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const float glast = sG[C - 1];
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb) {
+            FR fk[NST];
+#pragma unroll
+            for (int s = 0; s < NST; ++s)
+                fk[s] = make_frag<ET>(s, NBT, [&](int tb) { return frag_col<ET>(sK, LDK, 0, 16 * kb, tb, x, qd); });
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) S[kb][vb] *= glast;
 #pragma unroll
-            for (int s = 0; s < Steps<NBT, BLK>::n; ++s) {
-                FR fk = make_frag<ET>(s, NBT, [&](int tb) {
-                    return ld4<ET>(sKt + (16 * kb + x) * LDC + 16 * tb + 4 * qd); });
+            for (int s = 0; s < NST; ++s) {
 #pragma unroll
                 for (int vb = 0; vb < NB; ++vb) {
                     FR fd = make_frag<ET>(s, NBT, [&](int tb) { return Dpf[tb][vb]; });
-                    S[kb][vb] = mfma_step(fk, fd, S[kb][vb]);
+                    S[kb][vb] = mfma_step(fk[s], fd, S[kb][vb]);
                 }
             }
         }
         if (n + 1 < nchunks) {
             lds_barrier();                 // chunk n is done with LDS
-            stage(min(C, T - t0 - C), gcur, bcur);
+            stage(min(C, T - t0 - C), gcur);
         }
     }
 
