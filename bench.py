@@ -53,8 +53,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, TFLOP/s
 PREFILL = dict(B=8, T=8192, Hk=16, Hv=32, Dk=128, Dv=128, C=64, dtype="bf16")
 DECODE = dict(B=64, T=256, Hk=16, Hv=32, Dk=128, Dv=128, dtype="f16")
-CHUNK_KERNEL_SOURCES = ["gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_device.h",
-                        "gdn_chunk_bf16.hip"]
+CHUNK_KERNEL_SOURCES = ["gdn_chunk_pipe.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h",
+                        "gdn_device.h", "gdn_chunk_bf16.hip"]
+# the kernel that runs the long-prefill workload (bf16, Dk = Dv = 128, C = 64)
+CHUNK_KERNEL = "chunk_pipe_kernel"
+CHUNK_KERNEL_LABEL = "chunk_pipe_kernel<bf16,128,128,64>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_long_prefill_hbm_traffic.json")
 
 
@@ -125,10 +128,10 @@ def summarize_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib=102
     copy_fetch = pick(_counter_means(cfetch_dir, "FETCH_SIZE"), "copyBuffer")
     copy_write = pick(_counter_means(cwrite_dir, "WRITE_SIZE"), "copyBuffer")
     f_scale, w_scale = kib / copy_fetch, kib / copy_write
-    fetch = pick(_counter_means(fetch_dir, "FETCH_SIZE"), "chunk_fwd_kernel")
-    write = pick(_counter_means(write_dir, "WRITE_SIZE"), "chunk_fwd_kernel")
+    fetch = pick(_counter_means(fetch_dir, "FETCH_SIZE"), CHUNK_KERNEL)
+    write = pick(_counter_means(write_dir, "WRITE_SIZE"), CHUNK_KERNEL)
     rec = {
-        "kernel": "chunk_fwd_kernel<bf16,128,128,64>, long prefill",
+        "kernel": CHUNK_KERNEL_LABEL + ", long prefill",
         "source_hash": chunk_source_hash(),
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "copy_calibration_mib": copy_mib,
@@ -254,7 +257,7 @@ def main():
         "config": {"workload": "long_prefill", "B": P["B"], "T": P["T"], "Hk": P["Hk"],
                    "Hv": P["Hv"], "Dk": P["Dk"], "Dv": P["Dv"], "C": P["C"]},
         "roofline": {
-            "kernel": "chunk_fwd_kernel<bf16,128,128,64>",
+            "kernel": CHUNK_KERNEL_LABEL,
             "bound": "hbm",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,

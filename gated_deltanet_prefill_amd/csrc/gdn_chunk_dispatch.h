@@ -2,25 +2,39 @@
 #pragma once
 
 #include "gdn_chunk_impl.h"
+#include "gdn_chunk_pipe.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 template <typename ET, int DK, int DV, int C>
 hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
-    constexpr int NB = 2;                        // 32 value columns per wave
-    constexpr int DVS = DV;                      // one workgroup per slot
-    using L = ChunkCfg<ET, DK, DVS, C, NB>;
-    const int nsplit = DV / DVS;
-    const long nblocks = (long)a.B * a.Hv * nsplit;
+    const long nslots = (long)a.B * a.Hv;
     const int group = a.Hv / a.Hk;
-    const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
-    const dim3 grid((unsigned)nblocks), block(L::NT);
-    hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), grid, block, 0, st,
-                       static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
-                       static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale);
-    return hipGetLastError();
+    if constexpr (sizeof(ET) == 2 && DK == 128 && DV == 128 && C == 64) {
+        // the pipelined kernel: one 8-wave workgroup per slot
+        const int xcd_group = (group > 1 && nslots % (8L * group) == 0) ? group : 1;
+        hipLaunchKernelGGL((chunk_pipe_kernel<ET, DK, DV, C>), dim3((unsigned)nslots), dim3(512), 0, st,
+                           static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
+                           static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale);
+        return hipGetLastError();
+    } else {
+        // 32 value columns per wave for Dv = 128, else 16 (more waves, fewer
+        // live registers per wave at small Dv)
+        constexpr int NB = DV >= 128 ? 2 : 1;
+        constexpr int DVS = DV;                      // one workgroup per slot
+        using L = ChunkCfg<ET, DK, DVS, C, NB>;
+        const int nsplit = DV / DVS;
+        const long nblocks = nslots * nsplit;
+        const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
+        const dim3 grid((unsigned)nblocks), block(L::NT);
+        hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), grid, block, 0, st,
+                           static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
+                           static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale);
+        return hipGetLastError();
+    }
 }
 
 template <typename ET, int DK, int DV>

@@ -61,19 +61,17 @@ struct ChunkCfg {
     static constexpr int LDK = DK + EPU;              // sK, sQ
     static constexpr int LDV = DVS + EPU;             // sV
     static constexpr int LDC = C + EPU;               // sAn, sQKR (16-bit rows of C)
-    static constexpr int LDR = C + 4;                 // sR (f32)
     static constexpr int LDD = 16 + 4;                // sAd (f32 diagonal blocks)
     static constexpr int LDT = 16 + EPU;              // sTd (diagonal inverses)
     static constexpr int oK = 0;
     static constexpr int oQ = oK + C * LDK * ES;
     static constexpr int oV = oQ + C * LDK * ES;
-    static constexpr int oR = oV + C * LDV * ES;
-    static constexpr int oAn = oR + C * LDR * 4;
+    static constexpr int oAn = oV + C * LDV * ES;
     static constexpr int oQKR = oAn + C * LDC * ES;
     static constexpr int oAd = oQKR + C * LDC * ES;
     static constexpr int oTd = oAd + C * LDD * 4;
-    static constexpr int oVec = oTd + C * LDT * ES;   // beta, Sfx, G, Rlast
-    static constexpr int BYTES = oVec + 4 * C * 4;
+    static constexpr int oVec = oTd + C * LDT * ES;   // beta, g, P, Sfx, G, Rlast, block totals
+    static constexpr int BYTES = oVec + 7 * C * 4;
     // staging in 16-byte units
     static constexpr int UPK = DK / EPU;
     static constexpr int UPV = DVS / EPU;
@@ -160,6 +158,19 @@ __device__ __forceinline__ float quad_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xf, 0xf, false));
 }
 
+// Value of the lane S below / above within each row of 16 lanes (DPP
+// row_shr / row_shl); lanes without one get 1.
+template <int S>
+__device__ __forceinline__ float dpp_row_shr(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x110 + S, 0xf, 0xf, false));
+}
+template <int S>
+__device__ __forceinline__ float dpp_row_shl(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x100 + S, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -183,7 +194,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     using FR = typename Step<ET>::frag;
     constexpr int BLK = Step<ET>::BLK;
     constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT, NTPW = L::NTPW;
-    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDR = L::LDR, LDD = L::LDD,
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDD = L::LDD,
                   LDT = L::LDT, EPU = L::EPU;
     constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
     constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
@@ -192,15 +203,17 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     ET *sK = reinterpret_cast<ET *>(smem + L::oK);
     ET *sQ = reinterpret_cast<ET *>(smem + L::oQ);
     ET *sV = reinterpret_cast<ET *>(smem + L::oV);
-    float *sR = reinterpret_cast<float *>(smem + L::oR);
     ET *sAn = reinterpret_cast<ET *>(smem + L::oAn);    // -A (16-bit)
     ET *sQKR = reinterpret_cast<ET *>(smem + L::oQKR);
     float *sAd = reinterpret_cast<float *>(smem + L::oAd);  // diagonal blocks of A (f32)
     ET *sTd = reinterpret_cast<ET *>(smem + L::oTd);    // diagonal blocks of (I + A)^-1
     float *sb = reinterpret_cast<float *>(smem + L::oVec);
-    float *sSfx = sb + C;
+    float *sg = sb + C;
+    float *sP = sg + C;
+    float *sSfx = sP + C;
     float *sG = sSfx + C;
     float *sRl = sG + C;
+    float *sBT = sRl + C;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, x = lane & 15, qd = lane >> 4;
@@ -237,6 +250,10 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
         for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
 
+    // ---- -A and QKR above the diagonal blocks stay zero; clear them once
+    for (int i = tid; i < (L::oAd - L::oAn) / 16; i += NT)
+        reinterpret_cast<uint4 *>(smem + L::oAn)[i] = zero_u4();
+
     // ---- global -> register prefetch of one chunk.  Every load is issued
     // unconditionally from a clamped (always valid) row; rows past the end
     // of the sequence are zeroed when the registers are staged.
@@ -272,7 +289,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // Registers -> LDS (row-major K, Q, V; beta); rows t >= cn become zero,
     // g = 1, beta = 0.  The empty asm statements pin the point where the
     // prefetched values are first needed here, after the barrier.
-    auto stage = [&](int cn, float &gcur) {
+    auto stage = [&](int cn) {
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
             asm volatile("" : "+v"(rk[i].x), "+v"(rk[i].y), "+v"(rk[i].z), "+v"(rk[i].w));
@@ -282,13 +299,23 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         for (int i = 0; i < L::PERV; ++i)
             asm volatile("" : "+v"(rv[i].x), "+v"(rv[i].y), "+v"(rv[i].z), "+v"(rv[i].w));
         asm volatile("" : "+v"(rg), "+v"(rb));
+        if (cn < C) {                                  // tail chunk: zero the padded rows
+#pragma unroll
+            for (int i = 0; i < L::PERK; ++i) {
+                const int t = (tid + i * NT) / L::UPK;
+                if (t >= cn) { rk[i] = zero_u4(); rq[i] = zero_u4(); }
+            }
+#pragma unroll
+            for (int i = 0; i < L::PERV; ++i)
+                if ((tid + i * NT) / L::UPV >= cn) rv[i] = zero_u4();
+        }
 #pragma unroll
         for (int i = 0; i < L::PERK; ++i) {
             const int it = tid + i * NT;
             if (L::KIT % NT == 0 || it < L::KIT) {
                 const int t = it / L::UPK, u = it - t * L::UPK;
-                *reinterpret_cast<uint4 *>(sK + t * LDK + u * EPU) = (t < cn) ? rk[i] : zero_u4();
-                *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = (t < cn) ? rq[i] : zero_u4();
+                *reinterpret_cast<uint4 *>(sK + t * LDK + u * EPU) = rk[i];
+                *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = rq[i];
             }
         }
 #pragma unroll
@@ -296,21 +323,53 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             const int it = tid + i * NT;
             if (L::VIT % NT == 0 || it < L::VIT) {
                 const int t = it / L::UPV, u = it - t * L::UPV;
-                *reinterpret_cast<uint4 *>(sV + t * LDV + u * EPU) = (t < cn) ? rv[i] : zero_u4();
+                *reinterpret_cast<uint4 *>(sV + t * LDV + u * EPU) = rv[i];
             }
         }
-        gcur = (tid < cn) ? rg : 1.f;
-        if (tid < C) sb[tid] = (tid < cn) ? rb : 0.f;
+        // Gate products (wave 0, lane t holds g_t; g = 1 past the end):
+        // within each 16-token block (one DPP row) the inclusive prefix
+        // products P and the exclusive suffix products Sfx by four
+        // doubling steps; block totals BT; G[t] = P[t] * BT of earlier
+        // blocks; Rl[t] = R[c-1][t] = Sfx[t] * BT of later blocks.
+        if (wave == 0) {
+            const float gt = (tid < cn) ? rg : 1.f;
+            float p = gt, sx = gt;
+            p *= dpp_row_shr<1>(p);
+            p *= dpp_row_shr<2>(p);
+            p *= dpp_row_shr<4>(p);
+            p *= dpp_row_shr<8>(p);
+            sx *= dpp_row_shl<1>(sx);
+            sx *= dpp_row_shl<2>(sx);
+            sx *= dpp_row_shl<4>(sx);
+            sx *= dpp_row_shl<8>(sx);
+            const float sfx = dpp_row_shl<1>(sx);
+            const int bt = lane >> 4;
+            float gpre = p, rl = sfx;
+#pragma unroll
+            for (int bb = 0; bb < NBT; ++bb) {
+                const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 16 * bb + 15));
+                if (bb < bt) gpre *= tot;
+                if (bb > bt) rl *= tot;
+                if (lane == bb) sBT[bb] = tot;
+            }
+            if (lane < C) {
+                sb[lane] = (lane < cn) ? rb : 0.f;
+                sg[lane] = gt;
+                sP[lane] = p;
+                sSfx[lane] = sfx;
+                sG[lane] = gpre;
+                sRl[lane] = rl;
+            }
+        }
     };
 
     const int nchunks = (T + C - 1) / C;
     // chunk 0 is staged before the loop; inside, chunk n+1 is loaded into
     // registers at the top of iteration n and staged into LDS at its bottom,
     // once chunk n is done with LDS.
-    float gcur = 1.f;
     if (nchunks > 0) {
         prefetch(0);
-        stage(min(C, T), gcur);
+        stage(min(C, T));
     }
 
     for (int n = 0; n < nchunks; ++n) {
@@ -318,68 +377,6 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int cn = min(C, T - t0);
         if (n + 1 < nchunks) prefetch(t0 + C);
         lds_barrier();                     // chunk n staged
-
-        // ---- gates (wave 0, lane t holds g_t): products of decays only.
-        // P[t]: g over [block start, t]; Sfx[t]: over (t, block end];
-        // in-block ratios over (block start + j', t]; block totals BT;
-        // G[t] = P[t] * BT of earlier blocks; Rl[t] = Sfx[t] * BT of later
-        // ones; R[t][j] for an earlier block = P[t] * BT between * Sfx[j].
-        if (wave == 0) {
-            const int t = lane, bt = t >> 4, ti = t & 15, base = bt << 4;
-            const float gt = (t < C) ? gcur : 1.f;
-            float gb[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) gb[i] = __shfl(gt, base + i);
-            float p = 1.f, sx = 1.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i <= ti) p *= gb[i];
-                if (i > ti) sx *= gb[i];
-            }
-            if (t < C) sSfx[t] = sx;
-            f32x4 rin[4];
-            float r = 1.f;
-#pragma unroll
-            for (int jj = 15; jj >= 0; --jj) {
-                if (jj < ti) r *= gb[jj + 1];
-                rin[jj >> 2][jj & 3] = (jj <= ti) ? r : 0.f;
-            }
-            float btot[NBT];
-#pragma unroll
-            for (int bb = 0; bb < NBT; ++bb) btot[bb] = __shfl(p, 16 * bb + 15);
-            float gpre = p, rl = sx;
-#pragma unroll
-            for (int bb = 0; bb < NBT; ++bb) {
-                if (bb < bt) gpre *= btot[bb];
-                if (bb > bt) rl *= btot[bb];
-            }
-            if (t < C) {
-                sG[t] = gpre;
-                sRl[t] = rl;
-                // row t of R: blocks before t's own (products through the
-                // whole blocks in between), t's own block, zeros after
-                float m = p;                 // P[t] * BT(bt-1) * ... going left
-#pragma unroll
-                for (int jb = NBT - 1; jb >= 0; --jb) {
-                    f32x4 o[4];
-                    if (jb == bt) {
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) o[i4] = rin[i4];
-                    } else if (jb < bt) {
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4)
-                            o[i4] = *reinterpret_cast<const f32x4 *>(sSfx + 16 * jb + 4 * i4) * m;
-                    } else {
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) o[i4] = zero4();
-                    }
-                    if (jb < bt) m *= btot[jb];
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4)
-                        *reinterpret_cast<f32x4 *>(sR + t * LDR + 16 * jb + 4 * i4) = o[i4];
-                }
-            }
-        }
 
         // ---- one pass over the K and Q fragments:
         //   X = K S0^T (tiles [t][v]), Y^T = S0 Q^T (tiles [v][t]) for this
@@ -434,28 +431,49 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         }
         lds_barrier();
 
-        // ---- A = beta R (K K^T) strictly lower (as -A, 16-bit, and its
-        // diagonal blocks in f32); QKR = R (Q K^T) lower, incl. the diagonal
+        // ---- A = beta R (K K^T) strictly lower (stored as -A, 16-bit, and
+        // its diagonal blocks in f32); QKR = R (Q K^T) / sqrt(Dk), lower incl.
+        // the diagonal.  R[t][j] for j in an earlier block: P[t] x BT of the
+        // blocks between x Sfx[j]; in t's own block: g_{j+1} ... g_t by a
+        // running product.  Blocks above the diagonal keep their zeros.
 #pragma unroll
         for (int i = 0; i < NTPW; ++i) {
             const int tb = wave + i * NW;
             if (NBT % NW == 0 || tb < NBT) {
                 const int t = 16 * tb + x;
-                const float bt = sb[t];
+                const float bt = sb[t], pt = sP[t];
 #pragma unroll
                 for (int jb = 0; jb < NBT; ++jb) {
                     const int j0 = 16 * jb + 4 * qd;
-                    const f32x4 R = *reinterpret_cast<const f32x4 *>(sR + t * LDR + j0);
                     const f32x4 zk = tkk[i][jb], zq = tqk[i][jb];
-                    f32x4 a, o;
+                    if (jb < tb) {
+                        float m = pt;
+                        for (int bb = jb + 1; bb < tb; ++bb) m *= sBT[bb];
+                        const f32x4 R = *reinterpret_cast<const f32x4 *>(sSfx + j0) * m;
+                        st4<ET>(sAn + t * LDC + j0, cvt4<ET>(R * zk * (-bt)));
+                        st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(R * zq * scale));
+                    } else if (jb == tb) {
+                        const float *gblk = sg + 16 * tb;
+                        float acc = 1.f;                    // g over [4 qd + 4, x]
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        a[r] = (j0 + r < t) ? bt * (R[r] * zk[r]) : 0.f;
-                        o[r] = (j0 + r <= t) ? R[r] * zq[r] : 0.f;
+                        for (int ii = 1; ii < 16; ++ii)
+                            acc *= (ii >= 4 * qd + 4 && ii <= x) ? gblk[ii] : 1.f;
+                        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gblk + 4 * qd);
+                        f32x4 R;
+                        R[3] = acc;
+                        R[2] = (4 * qd + 3 <= x) ? R[3] * g4[3] : 1.f;
+                        R[1] = (4 * qd + 2 <= x) ? R[2] * g4[2] : 1.f;
+                        R[0] = (4 * qd + 1 <= x) ? R[1] * g4[1] : 1.f;
+                        f32x4 a, o;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            a[r] = (4 * qd + r < x) ? bt * (R[r] * zk[r]) : 0.f;
+                            o[r] = (4 * qd + r <= x) ? scale * (R[r] * zq[r]) : 0.f;
+                        }
+                        st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
+                        st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
+                        *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
                     }
-                    st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
-                    st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
-                    if (jb == tb) *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
                 }
             }
         }
@@ -533,10 +551,10 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
         }
 
-        // ---- Y^T = G (S0 Q^T) + D^T QKR^T  (intra-chunk term)
+        // ---- Y^T = G (S0 Q^T) / sqrt(Dk) + D^T QKR^T  (intra-chunk term; QKR carries 1/sqrt(Dk))
 #pragma unroll
         for (int tb = 0; tb < NBT; ++tb) {
-            const float gt = sG[16 * tb + x];
+            const float gt = sG[16 * tb + x] * scale;
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) Ya[vb][tb] *= gt;
             FR fr[NST];
@@ -563,7 +581,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             if (t < cn) {
                 ET *yrow = y + (((size_t)b * T + t0 + t) * Hv + hv) * Dv + vs * DVS + vloc + 4 * qd;
 #pragma unroll
-                for (int vb = 0; vb < NB; ++vb) st4<ET>(yrow + 16 * vb, cvt4<ET>(Ya[vb][tb] * scale));
+                for (int vb = 0; vb < NB; ++vb) st4<ET>(yrow + 16 * vb, cvt4<ET>(Ya[vb][tb]));
             }
         }
 
@@ -595,7 +613,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         }
         if (n + 1 < nchunks) {
             lds_barrier();                 // chunk n is done with LDS
-            stage(min(C, T - t0 - C), gcur);
+            stage(min(C, T - t0 - C));
         }
     }
 

@@ -1,0 +1,624 @@
+// gdn_chunk_pipe.h -- the software-pipelined chunk kernel for gfx950:
+// 16-bit q/k/v/y, Dk = Dv = 128, chunks of 64 tokens.
+//
+// The per-chunk work splits into a part that needs the running state and a
+// part that does not.  In the compact WY form of a chunk (metaltile-std
+// gated_delta_wy.rs page, module notes "Algorithm", steps 4-9: one unit lower
+// triangular solve turns the chunk's keys and values into pseudo-keys and
+// pseudo-values, and the state then enters only through products with them),
+// with the decay products of the ferrox-core gdn_chunk.rs page ("The
+// algebra": every ratio of decays is a product of decays):
+//
+//   A[t][j]   = beta_t R[t][j] k_t.k_j  (j < t),  T = (I + A)^-1
+//   W         = T diag(beta G) K,   U = T diag(beta) V         (state free)
+//   QKR[t][j] = R[t][j] q_t.k_j / sqrt(Dk)  (j <= t)            (state free)
+//   D         = U - W S^T           the true deltas d_t of the chunk
+//   y         = G (Q S^T) / sqrt(Dk) + QKR D
+//   S        <- G_last S + (diag(Rl) D)^T K,   Rl[t] = R[c-1][t]
+//
+// One workgroup of eight waves owns one (batch, value head) slot.  Waves 0-3
+// (state waves) keep the f32 state in registers, 32 value rows each.  Waves
+// 4-7 (prep waves) build the state-free matrices one chunk ahead and stage
+// the input two chunks ahead.  Each SIMD holds one wave of each kind, so the
+// matrix-core work of one overlaps the vector and LDS work of the other.
+// Iteration n has two phases, each closed by a workgroup barrier:
+//
+//   phase a   state: D = U_n + (-W_n) S^T, Y^T = S Q_n^T
+//             prep:  load V_{n+1}, K_{n+2}; K K^T, Q K^T tiles of chunk n+1
+//                    -> -A, QKR; diagonal blocks T_ii
+//   phase b   state: Y^T += D^T QKR^T, y, state update; U_{n+1} for its own
+//                    value columns (kept in registers for the next chunk)
+//             prep:  load Q_{n+2}; W_{n+1} (-W^T to LDS); gates of chunk n+2
+//
+// U and W come from blocked forward substitution over 16-token blocks,
+//   X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j).
+//
+// LDS layouts are swizzled so that the fragment reads and writes of each
+// buffer hit distinct banks: in the 256-byte rows of K and Q the 16-byte unit
+// u of row t sits at u ^ (t % 16); in the 128-byte rows of -W^T at
+// u ^ (k % 8); in the 128-byte rows of QKR and -A at u ^ ((t / 2) % 8).
+//
+// Lane x of value tile vb of state wave w holds value column
+//   32 w + 8 (x/4) + 4 vb + x%4,
+// so that one lane stores eight consecutive values of a y row at once.
+#pragma once
+
+#include "gdn_chunk_impl.h"
+
+namespace gdn {
+
+template <typename ET, int DK_, int DV_, int C_>
+struct PipeCfg {
+    static constexpr int DK = DK_, DV = DV_, C = C_;
+    static_assert(sizeof(ET) == 2, "16-bit element types only");
+    static_assert(DK == 128 && DV == 128 && C == 64, "the work split is written for this shape");
+    static constexpr int NBT = C / 16;      // 16-token blocks
+    static constexpr int NBK = DK / 16;     // 16-key blocks
+    static constexpr int NSK = DK / 32;     // contraction steps over keys
+    static constexpr int NB = 2;            // value tiles per state wave
+    // byte offsets
+    static constexpr unsigned KBUF = C * DK * 2;         // one chunk of K or Q
+    static constexpr unsigned oK = 0;                    // 3 x K
+    static constexpr unsigned oQ = oK + 3 * KBUF;        // 2 x Q
+    static constexpr unsigned VSL = C * 32 * 2;          // one 32-column V slice
+    static constexpr unsigned oV = oQ + 2 * KBUF;        // 4 x V slice [C][32]
+    static constexpr unsigned oW = oV + 4 * VSL;         // -W^T [DK][C]
+    static constexpr unsigned CBUF = C * C * 2;          // one C x C matrix
+    static constexpr unsigned oQKR = oW + DK * C * 2;    // 2 x QKR [C][C]
+    static constexpr unsigned oAn = oQKR + 2 * CBUF;     // -A [C][C]
+    static constexpr unsigned LDD = 20;                  // floats per row of Ad
+    static constexpr unsigned oAd = oAn + CBUF;          // A diagonal blocks [C][LDD] f32
+    static constexpr unsigned LDT = 24;                  // elements per row of Td
+    static constexpr unsigned oTd = oAd + C * LDD * 4;   // T diagonal blocks [C][LDT]
+    static constexpr unsigned NV = 7 * C;                // floats per gate-vector set
+    static constexpr unsigned oVec = oTd + C * LDT * 2;  // 3 x gate vectors
+    static constexpr unsigned BYTES = oVec + 3 * NV * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Gate-vector set of one chunk (floats): beta, g, in-block inclusive prefix
+// products P, in-block exclusive suffix products Sfx, G, Rl, block totals.
+enum { kVb = 0, kVg = 1, kVP = 2, kVSfx = 3, kVG = 4, kVRl = 5, kVBT = 6 };
+
+// Four 16-bit elements through gfx950's LDS transpose read: lane m of each
+// 16-lane group receives element m%4 of the 8-byte pieces addressed by lanes
+// m/4 + 4i, i = 0..3.  With lane j addressing row r0 + j/4 at column
+// c(j%4) .. +3, lane m receives column c(m/4) + m%4 of rows r0 .. r0+3.
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x4 ld_tr(const char *smem, unsigned byte) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(smem + byte));
+    return __builtin_bit_cast(typename Vec<ET>::x4, raw);
+}
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x4 lds4(const char *smem, unsigned byte) {
+    return *reinterpret_cast<const typename Vec<ET>::x4 *>(smem + byte);
+}
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x8 lds8(const char *smem, unsigned byte) {
+    return *reinterpret_cast<const typename Vec<ET>::x8 *>(smem + byte);
+}
+template <typename ET>
+__device__ __forceinline__ void sts4(char *smem, unsigned byte, typename Vec<ET>::x4 v) {
+    *reinterpret_cast<typename Vec<ET>::x4 *>(smem + byte) = v;
+}
+
+template <typename ET, int DK, int DV, int C>
+__global__ __launch_bounds__(512, 1)
+void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
+                       const ET *__restrict__ v, const float *__restrict__ g,
+                       const float *__restrict__ beta, const float *state_in,
+                       float *state_out, ET *__restrict__ y,
+                       int T, int Hk, int Hv, int xcd_group, float scale)
+{
+    using L = PipeCfg<ET, DK, DV, C>;
+    using X4 = typename Vec<ET>::x4;
+    using X8 = typename Vec<ET>::x8;
+    constexpr int NBT = L::NBT, NBK = L::NBK, NSK = L::NSK, NB = L::NB;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    auto Gv = [&](int i) { return reinterpret_cast<float *>(smem + L::oVec + i * L::NV * 4); };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wave & 3;                      // state wave index, or prep wave index p
+    const bool state_wave = wave < 4;
+    // Lane coordinates.  They pass through an empty asm statement at the top
+    // of every chunk, so the compiler forms lane-dependent addresses inside
+    // the loop (one or two instructions each) instead of holding dozens of
+    // precombined addresses in registers across it.
+    int lane = tid & 63, x = lane & 15, qd = lane >> 4;
+
+    // Workgroups are dealt round-robin over the 8 XCDs, so workgroups i and
+    // i + 8 share an XCD and its L2; with xcd_group = Hv/Hk > 1 they get
+    // value heads of the same key head, whose q/k stream is then fetched
+    // from HBM once per group.
+    int bid = blockIdx.x;
+    if (xcd_group > 1) {
+        const int xcd = bid & 7, kk = bid >> 3;
+        const int sib = kk % xcd_group, mm = kk / xcd_group;
+        bid = (mm * 8 + xcd) * xcd_group + sib;
+    }
+    const int hv = bid % Hv, b = bid / Hv, hk = hv / (Hv / Hk);
+    const int nchunks = (T + C - 1) / C;
+
+    // ---- lane-dependent LDS byte offsets (see the layout notes above)
+    // K/Q row fragment (16 bytes at unit 4s + qd of row 16b + x): ^ 64 s, + 4096 b
+    auto f_lKt = [&]() { return (unsigned)(x * 256 + (((qd ^ x) & 15) << 4)); };
+    // K/Q 8-byte halves at units 4s + qd/2 (+2) of row 16b + x: ^ (64 s [+32]), + 4096 b
+    auto f_lQh = [&]() { return (unsigned)(x * 256 + ((((qd >> 1) ^ x) & 15) << 4) + ((qd & 1) << 3)); };
+    // K transpose read, rows r0 + r4, columns 16 kb + 4 (x%4) ..: ^ 32 kb, + 256 r0
+    auto f_lKtr = [&]() {
+        const int r4 = 4 * qd + (x >> 2);
+        return (unsigned)(r4 * 256 + (((((x >> 1) & 1) ^ r4) & 15) << 4) + ((x & 1) << 3));
+    };
+    // -W^T, state side: transpose read rows k0 + r4, columns 16 tb + 4 (x%4): ^ 32 tb, + 128 k0
+    auto f_lWs = [&]() {
+        const int r4 = 4 * qd + (x >> 2);
+        return (unsigned)(r4 * 128 + ((((x >> 1) & 1) ^ (r4 & 7)) << 4) + ((x & 1) << 3));
+    };
+    // -W^T, prep side: write row k0 + x, 8 bytes at column 16 ib + 4 qd: ^ 32 ib, + 128 k0
+    auto f_lWp = [&]() { return (unsigned)(x * 128 + ((((qd >> 1) ^ (x & 7))) << 4) + ((qd & 1) << 3)); };
+    // QKR / -A rows 16 tb + x, 8 bytes at column 16 jb + 4 qd: ^ 32 jb, + 2048 tb
+    auto f_lA = [&]() { return (unsigned)(x * 128 + ((((qd >> 1) ^ (x >> 1)) & 7) << 4) + ((qd & 1) << 3)); };
+    // V slice of state wave w: transpose read rows 16 ib + r4, permuted
+    // columns 8 (m/4) + 4 vb + m%4: + 8 vb + 1024 ib
+    auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 64 + (x & 3) * 16); };
+
+    // ---------------- prep waves: global -> LDS loads ----------------
+    // Chunks of K, Q and V go from global memory straight into LDS
+    // (global_load_lds_dwordx4: lane l of the wave writes the 16 bytes at
+    // 16 l of a 1 KB block), so no staging registers are held across the
+    // loop.  The swizzle of K and Q is applied on the source side: the lane
+    // that fills position u' of row r fetches unit u' ^ (r % 16) of that row.
+    // Rows past the end of the sequence fetch the last row again; with
+    // g = 1 and beta = 0 there, those rows add nothing (A, W, U and D vanish
+    // on them, and their y rows are not stored).
+    const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * DV;
+    const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
+    const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
+    const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV + w * 32;
+    const float *gbase = g + (size_t)b * T * Hv + hv;
+    const float *bbase = beta + (size_t)b * T * Hv + hv;
+    // K/Q: prep wave p fills rows r = 16 p + 4 i + l/16 (i = 0..3), lane l
+    // fetching unit (l%16) ^ (r%16) = ((l%16) ^ (l/16)) ^ 4i; as an element
+    // offset (kstride is a multiple of 128): (okq0 ^ 32 i) + 4 i kstride.
+    // V: this wave's 32 columns, rows 16 i + l/4, 8 elements at 8 (l%4):
+    // ov0 + 16 i vstride.
+    auto f_okq0 = [&]() {
+        return (unsigned)((16 * w + qd) * kstride + 8 * ((lane & 15) ^ qd));
+    };
+    auto f_ov0 = [&]() { return (unsigned)((lane >> 2) * vstride + 8 * (lane & 3)); };
+    float rg = 1.f, rb = 0.f;
+    auto g2lds = [&](const ET *src, unsigned lds_byte) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(smem + lds_byte), 16, 0, 0);
+    };
+    auto issue_kq = [&](const ET *base, unsigned dst, int c) {
+        const int t0 = c * C;
+        const ET *src = base + (size_t)t0 * kstride;
+        if (t0 + C <= T) {
+            const unsigned o0 = f_okq0();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g2lds(src + ((o0 ^ (32 * i)) + 4 * i * kstride), dst + 4096 * w + 1024 * i);
+        } else {
+            const int last = T - t0 - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * w + 4 * i + (lane >> 4);
+                g2lds(src + (size_t)min(r, last) * kstride + 8 * ((lane & 15) ^ (r & 15)), dst + 4096 * w + 1024 * i);
+            }
+        }
+    };
+    auto issue_k = [&](int c) { issue_kq(kbase, L::oK + (c % 3) * L::KBUF, c); };
+    auto issue_q = [&](int c) { issue_kq(qbase, L::oQ + (c & 1) * L::KBUF, c); };
+    auto issue_v = [&](int c) {
+        const int t0 = c * C;
+        const ET *src = vbase + (size_t)t0 * vstride;
+        const unsigned dst = L::oV + w * L::VSL;
+        if (t0 + C <= T) {
+            const unsigned o0 = f_ov0();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g2lds(src + (o0 + 16 * i * vstride), dst + 1024 * i);
+        } else {
+            const int last = T - t0 - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                g2lds(src + (size_t)min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3), dst + 1024 * i);
+        }
+    };
+    // g and beta of chunk c into registers of prep wave 0 (lane = token)
+    auto load_gb = [&](int c) {
+        if (w == 0) {
+            const int t0 = c * C;
+            const size_t tg = (size_t)(t0 + min(lane, T - t0 - 1)) * Hv;
+            rg = gbase[tg];
+            rb = bbase[tg];
+        }
+    };
+    // Gate products of chunk c (prep wave 0, lane t holding g_t; g = 1 past
+    // the end): within each 16-token block (one DPP row) the inclusive prefix
+    // products P and the inclusive suffix products by four doubling steps;
+    // the exclusive suffix Sfx; block totals; G[t] = P[t] x totals of the
+    // earlier blocks; Rl[t] = Sfx[t] x totals of the later blocks.
+    auto scan_gates = [&](int c) {
+        if (w == 0) {
+            const int cn = min(C, T - c * C);
+            float *gv = Gv(c % 3);
+            const float gt = lane < cn ? rg : 1.f;
+            float p = gt, sx = gt;
+            p *= dpp_row_shr<1>(p);
+            p *= dpp_row_shr<2>(p);
+            p *= dpp_row_shr<4>(p);
+            p *= dpp_row_shr<8>(p);
+            sx *= dpp_row_shl<1>(sx);
+            sx *= dpp_row_shl<2>(sx);
+            sx *= dpp_row_shl<4>(sx);
+            sx *= dpp_row_shl<8>(sx);
+            const float sfx = dpp_row_shl<1>(sx);
+            const int bt = lane >> 4;
+            float gpre = p, rl = sfx;
+#pragma unroll
+            for (int bb = 0; bb < NBT; ++bb) {
+                const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 16 * bb + 15));
+                if (bb < bt) gpre *= tot;
+                if (bb > bt) rl *= tot;
+                if (lane == bb) gv[kVBT * C + bb] = tot;
+            }
+            gv[kVb * C + lane] = lane < cn ? rb : 0.f;
+            gv[kVg * C + lane] = gt;
+            gv[kVP * C + lane] = p;
+            gv[kVSfx * C + lane] = sfx;
+            gv[kVG * C + lane] = gpre;
+            gv[kVRl * C + lane] = rl;
+        }
+    };
+    static_assert(C == 64, "one lane per token in the gate scans");
+
+    // Blocked forward substitution for two 16-column tiles whose right-hand
+    // sides are rhs(ib, cb) (f32, lane x = column, rows 16 ib + 4 qd + r):
+    // X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j); emit(ib, cb, X_i f32).
+    // Returns the 16-bit blocks in Xf.
+    auto substitute = [&](unsigned lA, X4 (&Xf)[NBT][2], auto rhs, auto emit) {
+#pragma unroll
+        for (int ib = 0; ib < NBT; ++ib) {
+            f32x4 Z[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) Z[cb] = rhs(ib, cb);
+            // -A_ij X_j over j < ib: pairs of blocks, then an odd one
+#pragma unroll
+            for (int j = 0; j + 1 < ib; j += 2) {
+                const X8 fa = cat8<ET>(lds4<ET>(smem, L::oAn + ((lA ^ (32 * j)) + 2048 * ib)),
+                                       lds4<ET>(smem, L::oAn + ((lA ^ (32 * (j + 1))) + 2048 * ib)));
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) Z[cb] = mfma(fa, cat8<ET>(Xf[j][cb], Xf[j + 1][cb]), Z[cb]);
+            }
+            if (ib & 1) {
+                const X4 fa = lds4<ET>(smem, L::oAn + ((lA ^ (32 * (ib - 1))) + 2048 * ib));
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) Z[cb] = mfma(fa, Xf[ib - 1][cb], Z[cb]);
+            }
+            const X4 ft = lds4<ET>(smem, L::oTd + (16 * ib + x) * L::LDT * 2 + 8 * qd);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const f32x4 r = mfma(ft, cvt4<ET>(Z[cb]), zero4());
+                Xf[ib][cb] = cvt4<ET>(r);
+                emit(ib, cb, r);
+            }
+        }
+    };
+
+    // ---------------- state waves: the state ----------------
+    // S[kb][vb]: S^T tile, rows = keys 16 kb + 4 qd + r, columns = values.
+    f32x4 S[NBK][NB];
+    X4 Uf[NBT][NB];                              // U of the next chunk (own value columns)
+    const size_t sbase = (size_t)bid * DV * DK;
+    auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
+
+    if (state_wave) {
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb)
+                S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)vcol(vb, x) * DK + 16 * kb + 4 * qd)
+                                     : zero4();
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+    } else if (nchunks > 0) {
+        // chunk 0: K, Q and gates (its V comes in the first iteration)
+        load_gb(0);
+        issue_k(0);
+        issue_q(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        scan_gates(0);
+    }
+    // QKR blocks above the diagonal are never written: zero both buffers once.
+    for (int i = tid; i < (int)(2 * L::CBUF / 16); i += 512)
+        reinterpret_cast<uint4 *>(smem + L::oQKR)[i] = zero_u4();
+    lds_barrier();
+
+    for (int n = -1; n < nchunks; ++n) {
+        asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
+        if (state_wave) {
+            // ================= state waves =================
+            const unsigned lQh = f_lQh(), lKtr = f_lKtr(), lWs = f_lWs(), lA = f_lA(), lVs = f_lVs();
+            f32x4 D[NBT][NB], Y[NB][NBT];
+            if (n >= 0) {
+                // ---- phase a: D = U + (-W) S^T, Y^T = S Q^T
+                const unsigned qb = L::oQ + (n & 1) * L::KBUF;
+                const float *gv = Gv(n % 3);
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) {
+                        D[tb][vb] = to_f32x4<ET>(Uf[tb][vb]);
+                        Y[vb][tb] = zero4();
+                    }
+#pragma unroll
+                for (int s = 0; s < NSK; ++s) {
+                    X8 fs[NB];
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb)
+                        fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
+#pragma unroll
+                    for (int tb = 0; tb < NBT; ++tb) {
+                        const unsigned wa = L::oW + (lWs ^ (32 * tb)) + 128 * 32 * s;
+                        const X8 fw = cat8<ET>(ld_tr<ET>(smem, wa), ld_tr<ET>(smem, wa + 128 * 16));
+                        const X8 fq = cat8<ET>(lds4<ET>(smem, qb + (lQh ^ (64 * s)) + 4096 * tb),
+                                               lds4<ET>(smem, qb + (lQh ^ (64 * s + 32)) + 4096 * tb));
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb) {
+                            D[tb][vb] = mfma(fw, fs[vb], D[tb][vb]);
+                            Y[vb][tb] = mfma(fs[vb], fq, Y[vb][tb]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    const float gt = gv[kVG * C + 16 * tb + x] * scale;
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Y[vb][tb] *= gt;
+                }
+            }
+            lds_barrier();
+            if (n >= 0) {
+                // ---- phase b: Y^T += D^T QKR^T, y, S^T <- G_last S^T + K^T diag(Rl) D
+                const int t0 = n * C, cn = min(C, T - t0);
+                const unsigned kb_ = L::oK + (n % 3) * L::KBUF, rb_ = L::oQKR + (n & 1) * L::CBUF;
+                const float *gv = Gv(n % 3);
+                X4 Df[NBT][NB];
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Df[tb][vb] = cvt4<ET>(D[tb][vb]);
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    // QKR is zero above the diagonal blocks: pair blocks (0,1), (2,3)
+#pragma unroll
+                    for (int s = 0; 2 * s <= tb; ++s) {
+                        const X8 fr = cat8<ET>(lds4<ET>(smem, rb_ + (lA ^ (64 * s)) + 2048 * tb),
+                                               lds4<ET>(smem, rb_ + (lA ^ (64 * s + 32)) + 2048 * tb));
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            Y[vb][tb] = mfma(cat8<ET>(Df[2 * s][vb], Df[2 * s + 1][vb]), fr, Y[vb][tb]);
+                    }
+                }
+                // y: lane (x, qd) holds token 16 tb + x, values 32 w + 8 qd + (0..7)
+                ET *yc = y + (((size_t)b * T + t0) * Hv + hv) * DV + 32 * w + 8 * qd;
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    const int t = 16 * tb + x;
+                    if (t < cn)
+                        *reinterpret_cast<X8 *>(yc + (size_t)t * Hv * DV) = cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]));
+                }
+                X4 Dp[NBT][NB];
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    const f32x4 rl = *reinterpret_cast<const f32x4 *>(gv + kVRl * C + 16 * tb + 4 * qd);
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Dp[tb][vb] = cvt4<ET>(D[tb][vb] * rl);
+                }
+                const float glast = gv[kVG * C + C - 1];
+#pragma unroll
+                for (int kb = 0; kb < NBK; ++kb) {
+                    X8 fk[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const unsigned ka = kb_ + (lKtr ^ (32 * kb)) + 256 * 32 * s;
+                        fk[s] = cat8<ET>(ld_tr<ET>(smem, ka), ld_tr<ET>(smem, ka + 256 * 16));
+                    }
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) S[kb][vb] *= glast;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            S[kb][vb] = mfma(fk[s], cat8<ET>(Dp[2 * s][vb], Dp[2 * s + 1][vb]), S[kb][vb]);
+                }
+            }
+            if (n + 1 < nchunks) {
+                // ---- U of chunk n+1 for this wave's value columns: RHS = beta V,
+                // V read with the permuted columns of the value tiles.
+                const float *gv1 = Gv((n + 1) % 3);
+                const unsigned vsl = L::oV + w * L::VSL;
+                X4 Un[NBT][NB];
+                substitute(lA, Un,
+                    [&](int ib, int vb) {
+                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(gv1 + kVb * C + 16 * ib + 4 * qd);
+                        return to_f32x4<ET>(ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib)) * bv;
+                    },
+                    [&](int, int, f32x4) {});
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Uf[tb][vb] = Un[tb][vb];
+            }
+        } else {
+            // ================= prep waves =================
+            const int m = n + 1, p = w;
+            const unsigned lKt = f_lKt(), lKtr = f_lKtr(), lWp = f_lWp(), lA = f_lA();
+            // loads of this iteration, in issue order: g/beta of chunk m + 1,
+            // V of chunk m, K of chunk m + 1 (V is awaited before the phase
+            // barrier with the four K loads still in flight), then Q of chunk
+            // m + 1 in phase b (all awaited before the closing barrier)
+            if (m + 1 < nchunks) load_gb(m + 1);
+            if (m < nchunks) issue_v(m);
+            asm volatile("" ::: "memory");
+            if (m + 1 < nchunks) issue_k(m + 1);
+            if (m < nchunks) {
+                // ---- tiles of K K^T and Q K^T of chunk m; tile (jb, tb) has rows
+                // j = 16 jb + 4 qd + r and column t = 16 tb + x.  Prep wave p takes
+                // the diagonal tiles of block p and three of the twelve below it:
+                //   wave 0: KK(0,1) QK(0,1) KK(0,2)   wave 1: QK(0,2) KK(1,2) QK(1,2)
+                //   wave 2: KK(0,3) QK(0,3) KK(1,3)   wave 3: QK(1,3) KK(2,3) QK(2,3)
+                const unsigned kbm = L::oK + (m % 3) * L::KBUF, qbm = L::oQ + (m & 1) * L::KBUF;
+                const unsigned rbm = L::oQKR + (m & 1) * L::CBUF;
+                const float *gv = Gv(m % 3);
+                // tile i of wave p: block row jb, block column tb, from Q or K,
+                // packed two bits per field at 6 p + 2 i (one bit at 3 p + i for Q)
+                constexpr unsigned kJB = 0xa50500u, kTB = 0xfffaa5u, kQB = 0xaaau;
+                int tj[3], tt[3], tq[3];
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    tj[i] = (kJB >> (6 * p + 2 * i)) & 3;
+                    tt[i] = (kTB >> (6 * p + 2 * i)) & 3;
+                    tq[i] = (kQB >> (3 * p + i)) & 1;
+                }
+                f32x4 acc[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) acc[i] = zero4();
+#pragma unroll
+                for (int s = 0; s < NSK; ++s) {
+                    const unsigned lo = lKt ^ (64 * s);
+                    const X8 kp = lds8<ET>(smem, kbm + lo + 4096 * p);
+                    const X8 qp = lds8<ET>(smem, qbm + lo + 4096 * p);
+                    acc[0] = mfma(kp, kp, acc[0]);
+                    acc[1] = mfma(kp, qp, acc[1]);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        const X8 fa = lds8<ET>(smem, kbm + lo + 4096 * tj[i]);
+                        const X8 fb = lds8<ET>(smem, (tq[i] ? qbm : kbm) + lo + 4096 * tt[i]);
+                        acc[2 + i] = mfma(fa, fb, acc[2 + i]);
+                    }
+                }
+                // ---- diagonal block p: R[t][j] = g_{j+1} ... g_t inside the block;
+                // h = product of g over local indices [4 qd + 4, x] by an
+                // inclusive scan along the 16 lanes x of a DPP row.
+                {
+                    const int t = 16 * p + x;
+                    const float bt = gv[kVb * C + t];
+                    float h = (x >= 4 * qd + 4) ? gv[kVg * C + t] : 1.f;
+                    h *= dpp_row_shr<1>(h);
+                    h *= dpp_row_shr<2>(h);
+                    h *= dpp_row_shr<4>(h);
+                    h *= dpp_row_shr<8>(h);
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gv + kVg * C + 16 * p + 4 * qd);
+                    f32x4 R;
+                    R[3] = h;
+                    R[2] = (4 * qd + 3 <= x) ? R[3] * g4[3] : 1.f;
+                    R[1] = (4 * qd + 2 <= x) ? R[2] * g4[2] : 1.f;
+                    R[0] = (4 * qd + 1 <= x) ? R[1] * g4[1] : 1.f;
+                    f32x4 a, o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[0][r]) : 0.f;
+                        o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[1][r]) : 0.f;
+                    }
+                    const unsigned ao = (lA ^ (32 * p)) + 2048 * p;
+                    sts4<ET>(smem, L::oAn + ao, cvt4<ET>(-a));
+                    sts4<ET>(smem, rbm + ao, cvt4<ET>(o));
+                    *reinterpret_cast<f32x4 *>(smem + L::oAd + (t * L::LDD + 4 * qd) * 4) = a;
+                }
+                // ---- tiles below the diagonal: R[t][j] = P[t] x (totals of the
+                // blocks strictly between) x Sfx[j]
+                {
+                    const f32x4 tot = *reinterpret_cast<const f32x4 *>(gv + kVBT * C);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        const int jb = tj[i], tb = tt[i], t = 16 * tb + x;
+                        float mf = gv[kVP * C + t];
+#pragma unroll
+                        for (int bb = 1; bb < NBT - 1; ++bb) mf *= (bb > jb && bb < tb) ? tot[bb] : 1.f;
+                        const f32x4 R = *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * jb + 4 * qd) * mf;
+                        const unsigned ao = (lA ^ (32 * jb)) + 2048 * tb;
+                        if (tq[i]) sts4<ET>(smem, rbm + ao, cvt4<ET>(R * acc[2 + i] * scale));
+                        else sts4<ET>(smem, L::oAn + ao, cvt4<ET>(R * acc[2 + i] * (-gv[kVb * C + t])));
+                    }
+                }
+                // ---- T_pp = (I + A_pp)^-1 by f32 forward substitution: four
+                // lanes per column c, lane part pt holding rows pt, pt+4, pt+8,
+                // pt+12.  Column sweep: once x_j is final (it sits in part j%4),
+                // every later row subtracts A[i][j] x_j.  The rows come from this
+                // wave's own writes above (LDS keeps a wave's accesses in order).
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                {
+                    const int base = 16 * p;
+                    const int pt = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
+                    const float *ad = reinterpret_cast<const float *>(smem + L::oAd);
+                    f32x4 arow[4][4];
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4)
+                            arow[mm][j4] = *reinterpret_cast<const f32x4 *>(ad + (base + pt + 4 * mm) * L::LDD + 4 * j4);
+                    float sv[4];
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) sv[mm] = (pt + 4 * mm == c) ? 1.f : 0.f;
+#pragma unroll
+                    for (int j = 0; j < 15; ++j) {
+                        float xj;
+                        switch (j & 3) {
+                        case 0: xj = quad_bcast<0>(sv[j >> 2]); break;
+                        case 1: xj = quad_bcast<1>(sv[j >> 2]); break;
+                        case 2: xj = quad_bcast<2>(sv[j >> 2]); break;
+                        default: xj = quad_bcast<3>(sv[j >> 2]); break;
+                        }
+#pragma unroll
+                        for (int mm = 0; mm < 4; ++mm)
+                            if (4 * mm + 3 > j) sv[mm] -= arow[mm][j >> 2][j & 3] * xj;
+                    }
+                    ET *td = reinterpret_cast<ET *>(smem + L::oTd);
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) td[(base + pt + 4 * mm) * L::LDT + c] = from_f32<ET>(sv[mm]);
+                }
+            }
+            // V of chunk m has landed once no more than the four K loads are pending
+            if (m + 1 < nchunks) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (m + 1 < nchunks) issue_q(m + 1);
+            if (m < nchunks) {
+                // ---- W of chunk m, key columns 32 p + 16 cb + x: RHS = beta G K
+                const unsigned kbm = L::oK + (m % 3) * L::KBUF;
+                const float *gv = Gv(m % 3);
+                X4 Wf[NBT][2];
+                substitute(lA, Wf,
+                    [&](int ib, int cb) {
+                        const f32x4 bg = *reinterpret_cast<const f32x4 *>(gv + kVb * C + 16 * ib + 4 * qd) *
+                                         *reinterpret_cast<const f32x4 *>(gv + kVG * C + 16 * ib + 4 * qd);
+                        return to_f32x4<ET>(ld_tr<ET>(smem, kbm + (lKtr ^ (32 * (2 * p + cb))) + 4096 * ib)) * bg;
+                    },
+                    [&](int ib, int cb, f32x4 r) {
+                        sts4<ET>(smem, L::oW + (lWp ^ (32 * ib)) + 128 * (32 * p + 16 * cb), cvt4<ET>(-r));
+                    });
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (m + 1 < nchunks) scan_gates(m + 1);
+        }
+        lds_barrier();
+    }
+
+    // ---- the state, written once
+    if (state_wave) {
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb)
+                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + 16 * kb + 4 * qd) = S[kb][vb];
+    }
+}
+
+}  // namespace gdn
