@@ -23,9 +23,9 @@
 // matrix-core work of one overlaps the vector and LDS work of the other.
 // Iteration n has two phases, each closed by a workgroup barrier:
 //
-//   phase a   state: D = U_n + (-W_n) S^T, Y^T = S Q_n^T
-//             prep:  load V_{n+1}, K_{n+2}; K K^T, Q K^T tiles of chunk n+1
-//                    -> -A, QKR; diagonal blocks T_ii
+//   phase a   state: load V_{n+1}, K_{n+2}; D = U_n + (-W_n) S^T, Y^T = S Q_n^T
+//             prep:  K K^T, Q K^T tiles of chunk n+1 -> -A, QKR; diagonal
+//                    blocks T_ii
 //   phase b   state: Y^T += D^T QKR^T, y, state update; U_{n+1} for its own
 //                    value columns (kept in registers for the next chunk)
 //             prep:  load Q_{n+2}; W_{n+1} (-W^T to LDS); gates of chunk n+2
@@ -72,7 +72,8 @@ struct PipeCfg {
     static constexpr unsigned oTd = oAd + C * LDD * 4;   // T diagonal blocks [C][LDT]
     static constexpr unsigned NV = 7 * C;                // floats per gate-vector set
     static constexpr unsigned oVec = oTd + C * LDT * 2;  // 3 x gate vectors
-    static constexpr unsigned BYTES = oVec + 3 * NV * 4;
+    static constexpr unsigned oGB = oVec + 3 * NV * 4;   // g, beta of the next chunk, as loaded
+    static constexpr unsigned BYTES = oGB + 2 * C * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -170,7 +171,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // Chunks of K, Q and V go from global memory straight into LDS
     // (global_load_lds_dwordx4: lane l of the wave writes the 16 bytes at
     // 16 l of a 1 KB block), so no staging registers are held across the
-    // loop.  The swizzle of K and Q is applied on the source side: the lane
+    // loop.  The state waves load K and V in phase a, the prep waves Q in
+    // phase b (when its buffer is free); wave w of either kind fills K/Q rows
+    // 16 w .. 16 w + 15, state wave w the V columns 32 w .. 32 w + 31 that it
+    // reads itself.  The swizzle of K and Q is applied on the source side: the lane
     // that fills position u' of row r fetches unit u' ^ (r % 16) of that row.
     // Rows past the end of the sequence fetch the last row again; with
     // g = 1 and beta = 0 there, those rows add nothing (A, W, U and D vanish
@@ -181,7 +185,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV + w * 32;
     const float *gbase = g + (size_t)b * T * Hv + hv;
     const float *bbase = beta + (size_t)b * T * Hv + hv;
-    // K/Q: prep wave p fills rows r = 16 p + 4 i + l/16 (i = 0..3), lane l
+    // K/Q: wave w fills rows r = 16 w + 4 i + l/16 (i = 0..3), lane l
     // fetching unit (l%16) ^ (r%16) = ((l%16) ^ (l/16)) ^ 4i; as an element
     // offset (kstride is a multiple of 128): (okq0 ^ 32 i) + 4 i kstride.
     // V: this wave's 32 columns, rows 16 i + l/4, 8 elements at 8 (l%4):
@@ -190,10 +194,19 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         return (unsigned)((16 * w + qd) * kstride + 8 * ((lane & 15) ^ qd));
     };
     auto f_ov0 = [&]() { return (unsigned)((lane >> 2) * vstride + 8 * (lane & 3)); };
-    float rg = 1.f, rb = 0.f;
-    auto g2lds = [&](const ET *src, unsigned lds_byte) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                         (__attribute__((address_space(3))) void *)(smem + lds_byte), 16, 0, 0);
+    // One 1 KB block: lane l fetches the 16 bytes at src + off (off in
+    // bytes, per lane; src uniform) into LDS at lds_byte + 16 l.  Written as
+    // inline assembly: the compiler would otherwise make the wave wait for
+    // the whole transfer before its next LDS read.  Completion is awaited
+    // explicitly (s_waitcnt vmcnt) before the barrier that publishes it.
+    const unsigned lds_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
+    auto g2lds = [&](const ET *src, unsigned off, unsigned lds_byte) {
+        const unsigned la = __builtin_amdgcn_readfirstlane(lds_base + lds_byte);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(src), "s"(la) : "memory", "m0");
+#pragma clang diagnostic pop
     };
     auto issue_kq = [&](const ET *base, unsigned dst, int c) {
         const int t0 = c * C;
@@ -201,13 +214,13 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (t0 + C <= T) {
             const unsigned o0 = f_okq0();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g2lds(src + ((o0 ^ (32 * i)) + 4 * i * kstride), dst + 4096 * w + 1024 * i);
+            for (int i = 0; i < 4; ++i) g2lds(src, 2 * ((o0 ^ (32 * i)) + 4 * i * (unsigned)kstride), dst + 4096 * w + 1024 * i);
         } else {
             const int last = T - t0 - 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * w + 4 * i + (lane >> 4);
-                g2lds(src + (size_t)min(r, last) * kstride + 8 * ((lane & 15) ^ (r & 15)), dst + 4096 * w + 1024 * i);
+                g2lds(src, 2 * (unsigned)(min(r, last) * kstride + 8 * ((lane & 15) ^ (r & 15))), dst + 4096 * w + 1024 * i);
             }
         }
     };
@@ -220,21 +233,30 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (t0 + C <= T) {
             const unsigned o0 = f_ov0();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g2lds(src + (o0 + 16 * i * vstride), dst + 1024 * i);
+            for (int i = 0; i < 4; ++i) g2lds(src, 2 * (o0 + 16 * i * (unsigned)vstride), dst + 1024 * i);
         } else {
             const int last = T - t0 - 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                g2lds(src + (size_t)min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3), dst + 1024 * i);
+                g2lds(src, 2 * (unsigned)(min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3)), dst + 1024 * i);
         }
     };
-    // g and beta of chunk c into registers of prep wave 0 (lane = token)
+    // g and beta of chunk c into LDS (prep wave 0; lane = token, rows past
+    // the end read the last row)
     auto load_gb = [&](int c) {
         if (w == 0) {
             const int t0 = c * C;
-            const size_t tg = (size_t)(t0 + min(lane, T - t0 - 1)) * Hv;
-            rg = gbase[tg];
-            rb = bbase[tg];
+            const unsigned off = 4 * (unsigned)(min(lane, T - t0 - 1) * Hv);
+            const float *gc = gbase + (size_t)t0 * Hv, *bc = bbase + (size_t)t0 * Hv;
+            const unsigned lg = __builtin_amdgcn_readfirstlane(lds_base + L::oGB);
+            const unsigned lb = __builtin_amdgcn_readfirstlane(lds_base + L::oGB + C * 4);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                         :: "v"(off), "s"(gc), "s"(lg) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                         :: "v"(off), "s"(bc), "s"(lb) : "memory", "m0");
+#pragma clang diagnostic pop
         }
     };
     // Gate products of chunk c (prep wave 0, lane t holding g_t; g = 1 past
@@ -244,6 +266,9 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // earlier blocks; Rl[t] = Sfx[t] x totals of the later blocks.
     auto scan_gates = [&](int c) {
         if (w == 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const float rg = reinterpret_cast<const float *>(smem + L::oGB)[lane];
+            const float rb = reinterpret_cast<const float *>(smem + L::oGB)[C + lane];
             const int cn = min(C, T - c * C);
             float *gv = Gv(c % 3);
             const float gt = lane < cn ? rg : 1.f;
@@ -317,6 +342,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
 
     if (state_wave) {
+        if (nchunks > 0) {
+            issue_k(0);
+            issue_q(0);
+        }
 #pragma unroll
         for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
@@ -327,12 +356,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
-    } else if (nchunks > 0) {
-        // chunk 0: K, Q and gates (its V comes in the first iteration)
-        load_gb(0);
-        issue_k(0);
-        issue_q(0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (nchunks > 0) {
+        // gates of chunk 0 (its V comes in the first iteration)
+        load_gb(0);
         scan_gates(0);
     }
     // QKR blocks above the diagonal are never written: zero both buffers once.
@@ -345,6 +372,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (state_wave) {
             // ================= state waves =================
             const unsigned lQh = f_lQh(), lKtr = f_lKtr(), lWs = f_lWs(), lA = f_lA(), lVs = f_lVs();
+            // K of chunk n+2 and V of chunk n+1, both awaited before the phase
+            // barrier (V is read in phase b, K by the prep waves next chunk)
+            if (n + 2 < nchunks) issue_k(n + 2);
+            if (n + 1 < nchunks) issue_v(n + 1);
             f32x4 D[NBT][NB], Y[NB][NBT];
             if (n >= 0) {
                 // ---- phase a: D = U + (-W) S^T, Y^T = S Q^T
@@ -383,6 +414,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     for (int vb = 0; vb < NB; ++vb) Y[vb][tb] *= gt;
                 }
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
             if (n >= 0) {
                 // ---- phase b: Y^T += D^T QKR^T, y, S^T <- G_last S^T + K^T diag(Rl) D
@@ -460,14 +492,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // ================= prep waves =================
             const int m = n + 1, p = w;
             const unsigned lKt = f_lKt(), lKtr = f_lKtr(), lWp = f_lWp(), lA = f_lA();
-            // loads of this iteration, in issue order: g/beta of chunk m + 1,
-            // V of chunk m, K of chunk m + 1 (V is awaited before the phase
-            // barrier with the four K loads still in flight), then Q of chunk
-            // m + 1 in phase b (all awaited before the closing barrier)
             if (m + 1 < nchunks) load_gb(m + 1);
-            if (m < nchunks) issue_v(m);
-            asm volatile("" ::: "memory");
-            if (m + 1 < nchunks) issue_k(m + 1);
             if (m < nchunks) {
                 // ---- tiles of K K^T and Q K^T of chunk m; tile (jb, tb) has rows
                 // j = 16 jb + 4 qd + r and column t = 16 tb + x.  Prep wave p takes
@@ -585,10 +610,8 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     for (int mm = 0; mm < 4; ++mm) td[(base + pt + 4 * mm) * L::LDT + c] = from_f32<ET>(sv[mm]);
                 }
             }
-            // V of chunk m has landed once no more than the four K loads are pending
-            if (m + 1 < nchunks) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
+            // Q of chunk m + 1 (its buffer held Q of chunk m - 1, read in phase a)
             if (m + 1 < nchunks) issue_q(m + 1);
             if (m < nchunks) {
                 // ---- W of chunk m, key columns 32 p + 16 cb + x: RHS = beta G K
@@ -605,8 +628,8 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         sts4<ET>(smem, L::oW + (lWp ^ (32 * ib)) + 128 * (32 * p + 16 * cb), cvt4<ET>(-r));
                     });
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (m + 1 < nchunks) scan_gates(m + 1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         lds_barrier();
     }
