@@ -28,19 +28,26 @@
 //                    blocks T_ii
 //   phase b   state: Y^T += D^T QKR^T, y, state update; U_{n+1} for its own
 //                    value columns (kept in registers for the next chunk)
-//             prep:  load Q_{n+2}; W_{n+1} (-W^T to LDS); gates of chunk n+2
+//             prep:  load Q_{n+2}; W_{n+1} (-W to LDS); gates of chunk n+2
 //
 // U and W come from blocked forward substitution over 16-token blocks,
 //   X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j).
 //
 // LDS layouts are swizzled so that the fragment reads and writes of each
-// buffer hit distinct banks: in the 256-byte rows of K and Q the 16-byte unit
-// u of row t sits at u ^ (t % 16); in the 128-byte rows of -W^T at
-// u ^ (k % 8); in the 128-byte rows of QKR and -A at u ^ ((t / 2) % 8).
+// buffer hit distinct banks: in the 256-byte rows of K, Q and -W (token rows,
+// keys along the row) the 16-byte unit u of row t sits at u ^ (t % 16); in
+// the 128-byte rows of QKR and -A at u ^ ((t / 2) % 8).  In QKR and -A,
+// column j = 32 s + 16 h + 4 q + r sits at position 32 s + 8 q + 4 h + r, so
+// that the 4-column pieces of blocks 2 s and 2 s + 1 that one lane holds
+// are adjacent.
 //
 // Lane x of value tile vb of state wave w holds value column
 //   32 w + 8 (x/4) + 4 vb + x%4,
-// so that one lane stores eight consecutive values of a y row at once.
+// so that one lane stores eight consecutive values of a y row at once.  Row
+// 4 qd + r of key tile kb = 2 s + h of the state holds key
+//   32 s + 8 qd + 4 h + r,
+// so that the two tiles of a 32-key step give each lane eight consecutive
+// keys: the -W and Q operands of that step are then single 16-byte reads.
 #pragma once
 
 #include "gdn_chunk_impl.h"
@@ -62,7 +69,7 @@ struct PipeCfg {
     static constexpr unsigned oQ = oK + 3 * KBUF;        // 2 x Q
     static constexpr unsigned VSL = C * 32 * 2;          // one 32-column V slice
     static constexpr unsigned oV = oQ + 2 * KBUF;        // 4 x V slice [C][32]
-    static constexpr unsigned oW = oV + 4 * VSL;         // -W^T [DK][C]
+    static constexpr unsigned oW = oV + 4 * VSL;         // -W [C][DK]
     static constexpr unsigned CBUF = C * C * 2;          // one C x C matrix
     static constexpr unsigned oQKR = oW + DK * C * 2;    // 2 x QKR [C][C]
     static constexpr unsigned oAn = oQKR + 2 * CBUF;     // -A [C][C]
@@ -145,24 +152,28 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const int nchunks = (T + C - 1) / C;
 
     // ---- lane-dependent LDS byte offsets (see the layout notes above)
-    // K/Q row fragment (16 bytes at unit 4s + qd of row 16b + x): ^ 64 s, + 4096 b
+    // K/Q/-W row fragment (16 bytes at unit 4s + qd of row 16b + x): ^ 64 s, + 4096 b
     auto f_lKt = [&]() { return (unsigned)(x * 256 + (((qd ^ x) & 15) << 4)); };
-    // K/Q 8-byte halves at units 4s + qd/2 (+2) of row 16b + x: ^ (64 s [+32]), + 4096 b
-    auto f_lQh = [&]() { return (unsigned)(x * 256 + ((((qd >> 1) ^ x) & 15) << 4) + ((qd & 1) << 3)); };
     // K transpose read, rows r0 + r4, columns 16 kb + 4 (x%4) ..: ^ 32 kb, + 256 r0
     auto f_lKtr = [&]() {
         const int r4 = 4 * qd + (x >> 2);
         return (unsigned)(r4 * 256 + (((((x >> 1) & 1) ^ r4) & 15) << 4) + ((x & 1) << 3));
     };
-    // -W^T, state side: transpose read rows k0 + r4, columns 16 tb + 4 (x%4): ^ 32 tb, + 128 k0
-    auto f_lWs = [&]() {
+    // K transpose read for the state update, rows r0 + r4, keys 32 s + 4 h +
+    // 8 (x%4) .. +3 (lane x then receives key 32 s + 4 h + 8 (x/4) + x%4):
+    // ^ 64 s, + 8 h, + 256 r0
+    auto f_lKu = [&]() {
         const int r4 = 4 * qd + (x >> 2);
-        return (unsigned)(r4 * 128 + ((((x >> 1) & 1) ^ (r4 & 7)) << 4) + ((x & 1) << 3));
+        return (unsigned)(r4 * 256 + ((((x & 3) ^ r4) & 15) << 4));
     };
-    // -W^T, prep side: write row k0 + x, 8 bytes at column 16 ib + 4 qd: ^ 32 ib, + 128 k0
-    auto f_lWp = [&]() { return (unsigned)(x * 128 + ((((qd >> 1) ^ (x & 7))) << 4) + ((qd & 1) << 3)); };
-    // QKR / -A rows 16 tb + x, 8 bytes at column 16 jb + 4 qd: ^ 32 jb, + 2048 tb
-    auto f_lA = [&]() { return (unsigned)(x * 128 + ((((qd >> 1) ^ (x >> 1)) & 7) << 4) + ((qd & 1) << 3)); };
+    // -W, prep side: element (t = 16 ib + 4 qd + r, key 32 p + 16 cb + x), 2
+    // bytes: (this ^ (r << 4) ^ (64 p + 32 cb)) + 256 r + 4096 ib
+    auto f_lWp = [&]() { return (unsigned)(4 * qd * 256 + ((((x >> 3) ^ (4 * qd)) & 15) << 4) + 2 * (x & 7)); };
+    // QKR / -A rows 16 tb + x, the 4 columns 16 jb + 4 qd ..:
+    //   (this ^ 64 (jb/2)) + 8 (jb%2) + 2048 tb;
+    // the 8 columns of blocks 2 s, 2 s + 1 that lane (x, qd) holds: ^ 64 s
+    auto f_lA = [&]() { return (unsigned)(x * 128 + (((qd ^ (x >> 1)) & 7) << 4)); };
+    auto aoff = [](unsigned lA, int jb, int tb) { return (lA ^ (64 * (jb >> 1))) + 8 * (jb & 1) + 2048 * tb; };
     // V slice of state wave w: transpose read rows 16 ib + r4, permuted
     // columns 8 (m/4) + 4 vb + m%4: + 8 vb + 1024 ib
     auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 64 + (x & 3) * 16); };
@@ -311,18 +322,18 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             f32x4 Z[2];
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) Z[cb] = rhs(ib, cb);
-            // -A_ij X_j over j < ib: pairs of blocks, then an odd one
+            // -A_ij X_j over j < ib, two blocks per 16x16x32 product; an odd
+            // last block is paired with the diagonal block and a zero X.  Every
+            // product into Z has the same shape: on gfx950 a 16x16x32 result
+            // fed to a 16x16x16 accumulator (or back) needs five independent
+            // issue slots in between, which the compiler does not always
+            // insert; same-shape chains are interlocked by the hardware.
 #pragma unroll
-            for (int j = 0; j + 1 < ib; j += 2) {
-                const X8 fa = cat8<ET>(lds4<ET>(smem, L::oAn + ((lA ^ (32 * j)) + 2048 * ib)),
-                                       lds4<ET>(smem, L::oAn + ((lA ^ (32 * (j + 1))) + 2048 * ib)));
+            for (int j = 0; j < ib; j += 2) {
+                const X8 fa = lds8<ET>(smem, L::oAn + (lA ^ (32 * j)) + 2048 * ib);
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) Z[cb] = mfma(fa, cat8<ET>(Xf[j][cb], Xf[j + 1][cb]), Z[cb]);
-            }
-            if (ib & 1) {
-                const X4 fa = lds4<ET>(smem, L::oAn + ((lA ^ (32 * (ib - 1))) + 2048 * ib));
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) Z[cb] = mfma(fa, Xf[ib - 1][cb], Z[cb]);
+                for (int cb = 0; cb < 2; ++cb)
+                    Z[cb] = mfma(fa, cat8<ET>(Xf[j][cb], j + 1 < ib ? Xf[j + 1][cb] : X4{}), Z[cb]);
             }
             const X4 ft = lds4<ET>(smem, L::oTd + (16 * ib + x) * L::LDT * 2 + 8 * qd);
 #pragma unroll
@@ -335,11 +346,12 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     };
 
     // ---------------- state waves: the state ----------------
-    // S[kb][vb]: S^T tile, rows = keys 16 kb + 4 qd + r, columns = values.
+    // S[kb][vb]: S^T tile, rows = keys kcol(kb, qd) + r, columns = values.
     f32x4 S[NBK][NB];
     X4 Uf[NBT][NB];                              // U of the next chunk (own value columns)
     const size_t sbase = (size_t)bid * DV * DK;
     auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
+    auto kcol = [&](int kb, int q4) { return 32 * (kb >> 1) + 8 * q4 + 4 * (kb & 1); };
 
     if (state_wave) {
         if (nchunks > 0) {
@@ -350,7 +362,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
             for (int kb = 0; kb < NBK; ++kb)
-                S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)vcol(vb, x) * DK + 16 * kb + 4 * qd)
+                S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd))
                                      : zero4();
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
@@ -371,7 +383,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
         if (state_wave) {
             // ================= state waves =================
-            const unsigned lQh = f_lQh(), lKtr = f_lKtr(), lWs = f_lWs(), lA = f_lA(), lVs = f_lVs();
+            const unsigned lKt = f_lKt(), lKu = f_lKu(), lA = f_lA(), lVs = f_lVs();
             // K of chunk n+2 and V of chunk n+1, both awaited before the phase
             // barrier (V is read in phase b, K by the prep waves next chunk)
             if (n + 2 < nchunks) issue_k(n + 2);
@@ -390,16 +402,16 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
 #pragma unroll
                 for (int s = 0; s < NSK; ++s) {
+                    // keys 32 s + 8 qd + (0..7) in lane (x, qd) of every operand
                     X8 fs[NB];
 #pragma unroll
                     for (int vb = 0; vb < NB; ++vb)
                         fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
 #pragma unroll
                     for (int tb = 0; tb < NBT; ++tb) {
-                        const unsigned wa = L::oW + (lWs ^ (32 * tb)) + 128 * 32 * s;
-                        const X8 fw = cat8<ET>(ld_tr<ET>(smem, wa), ld_tr<ET>(smem, wa + 128 * 16));
-                        const X8 fq = cat8<ET>(lds4<ET>(smem, qb + (lQh ^ (64 * s)) + 4096 * tb),
-                                               lds4<ET>(smem, qb + (lQh ^ (64 * s + 32)) + 4096 * tb));
+                        const unsigned lo = (lKt ^ (64 * s)) + 4096 * tb;
+                        const X8 fw = lds8<ET>(smem, L::oW + lo);
+                        const X8 fq = lds8<ET>(smem, qb + lo);
 #pragma unroll
                         for (int vb = 0; vb < NB; ++vb) {
                             D[tb][vb] = mfma(fw, fs[vb], D[tb][vb]);
@@ -431,8 +443,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     // QKR is zero above the diagonal blocks: pair blocks (0,1), (2,3)
 #pragma unroll
                     for (int s = 0; 2 * s <= tb; ++s) {
-                        const X8 fr = cat8<ET>(lds4<ET>(smem, rb_ + (lA ^ (64 * s)) + 2048 * tb),
-                                               lds4<ET>(smem, rb_ + (lA ^ (64 * s + 32)) + 2048 * tb));
+                        const X8 fr = lds8<ET>(smem, rb_ + (lA ^ (64 * s)) + 2048 * tb);
 #pragma unroll
                         for (int vb = 0; vb < NB; ++vb)
                             Y[vb][tb] = mfma(cat8<ET>(Df[2 * s][vb], Df[2 * s + 1][vb]), fr, Y[vb][tb]);
@@ -459,7 +470,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     X8 fk[2];
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const unsigned ka = kb_ + (lKtr ^ (32 * kb)) + 256 * 32 * s;
+                        const unsigned ka = kb_ + (lKu ^ (64 * (kb >> 1))) + 8 * (kb & 1) + 256 * 32 * s;
                         fk[s] = cat8<ET>(ld_tr<ET>(smem, ka), ld_tr<ET>(smem, ka + 256 * 16));
                     }
 #pragma unroll
@@ -552,7 +563,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[0][r]) : 0.f;
                         o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[1][r]) : 0.f;
                     }
-                    const unsigned ao = (lA ^ (32 * p)) + 2048 * p;
+                    const unsigned ao = aoff(lA, p, p);
                     sts4<ET>(smem, L::oAn + ao, cvt4<ET>(-a));
                     sts4<ET>(smem, rbm + ao, cvt4<ET>(o));
                     *reinterpret_cast<f32x4 *>(smem + L::oAd + (t * L::LDD + 4 * qd) * 4) = a;
@@ -568,7 +579,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                         for (int bb = 1; bb < NBT - 1; ++bb) mf *= (bb > jb && bb < tb) ? tot[bb] : 1.f;
                         const f32x4 R = *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * jb + 4 * qd) * mf;
-                        const unsigned ao = (lA ^ (32 * jb)) + 2048 * tb;
+                        const unsigned ao = aoff(lA, jb, tb);
                         if (tq[i]) sts4<ET>(smem, rbm + ao, cvt4<ET>(R * acc[2 + i] * scale));
                         else sts4<ET>(smem, L::oAn + ao, cvt4<ET>(R * acc[2 + i] * (-gv[kVb * C + t])));
                     }
@@ -625,7 +636,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         return to_f32x4<ET>(ld_tr<ET>(smem, kbm + (lKtr ^ (32 * (2 * p + cb))) + 4096 * ib)) * bg;
                     },
                     [&](int ib, int cb, f32x4 r) {
-                        sts4<ET>(smem, L::oW + (lWp ^ (32 * ib)) + 128 * (32 * p + 16 * cb), cvt4<ET>(-r));
+                        const X4 wv = cvt4<ET>(-r);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            *reinterpret_cast<ET *>(smem + L::oW + ((lWp ^ (rr << 4) ^ (64 * p + 32 * cb)) + 256 * rr + 4096 * ib)) = wv[rr];
                     });
             }
             if (m + 1 < nchunks) scan_gates(m + 1);
@@ -640,7 +654,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
             for (int kb = 0; kb < NBK; ++kb)
-                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + 16 * kb + 4 * qd) = S[kb][vb];
+                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd)) = S[kb][vb];
     }
 }
 

@@ -101,6 +101,26 @@ def test_vanishing_decay(gpu_lib, gval):
     assert_parity(y, s, yr, sr, "bf16", f"g={gval}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_no_decay_repeated(gpu_lib, dtype):
+    """g = 1 (the plain delta rule): no decay shrinks the couplings between
+    distant tokens, so an error in any block of the triangular solve shows up
+    at full size.  Several chunks and a ragged tail, the 128-dimensional
+    heads of the pipelined kernel, three runs that must agree bit for bit."""
+    inp = gi.make_inputs(2, 200, 2, 4, 128, 128, dtype, gate="const", gate_const=1.0,
+                         state_std=0.05, seed=4)
+    d = upload(inp)
+    outs = []
+    for _ in range(3):
+        y, s = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=64)
+        torch.cuda.synchronize()
+        outs.append((y.clone(), s.clone()))
+    for y, s in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(s, outs[0][1])
+    yr, sr = oracle_run(inp)
+    assert_parity(to_host_f64(outs[0][0]), to_host_f64(outs[0][1]), yr, sr, dtype, f"g=1 {dtype}")
+
+
 def test_in_place_state(gpu_lib):
     inp = gi.make_inputs(2, 90, 2, 4, 128, 128, "bf16", gate="sigmoid", state_std=0.1, seed=9)
     d = upload(inp)
