@@ -23,12 +23,13 @@
 // matrix-core work of one overlaps the vector and LDS work of the other.
 // Iteration n has two phases, each closed by a workgroup barrier:
 //
-//   phase a   state: load V_{n+1}, K_{n+2}; D = U_n + (-W_n) S^T, Y^T = S Q_n^T
+//   phase a   state: load V_{n+1}, K_{n+2}, g and beta of n+2; D = U_n +
+//                    (-W_n) S^T, Y^T = S Q_n^T; gate products of chunk n+2
 //             prep:  K K^T, Q K^T tiles of chunk n+1 -> -A, QKR; diagonal
 //                    blocks T_ii
 //   phase b   state: Y^T += D^T QKR^T, y, state update; U_{n+1} for its own
 //                    value columns (kept in registers for the next chunk)
-//             prep:  load Q_{n+2}; W_{n+1} (-W to LDS); gates of chunk n+2
+//             prep:  load Q_{n+2}; W_{n+1} (-W to LDS)
 //
 // U and W come from blocked forward substitution over 16-token blocks,
 //   X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j).
@@ -219,21 +220,20 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                      :: "v"(off), "s"(src), "s"(la) : "memory", "m0");
 #pragma clang diagnostic pop
     };
-    auto issue_kq = [&](const ET *base, unsigned dst, int c) {
+    // block i (rows 16 w + 4 i ..) of this wave's share of a K or Q chunk
+    auto issue_kq_blk = [&](const ET *base, unsigned dst, int c, int i) {
         const int t0 = c * C;
         const ET *src = base + (size_t)t0 * kstride;
         if (t0 + C <= T) {
-            const unsigned o0 = f_okq0();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) g2lds(src, 2 * ((o0 ^ (32 * i)) + 4 * i * (unsigned)kstride), dst + 4096 * w + 1024 * i);
+            g2lds(src, 2 * ((f_okq0() ^ (32 * i)) + 4 * i * (unsigned)kstride), dst + 4096 * w + 1024 * i);
         } else {
-            const int last = T - t0 - 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * w + 4 * i + (lane >> 4);
-                g2lds(src, 2 * (unsigned)(min(r, last) * kstride + 8 * ((lane & 15) ^ (r & 15))), dst + 4096 * w + 1024 * i);
-            }
+            const int r = 16 * w + 4 * i + (lane >> 4);
+            g2lds(src, 2 * (unsigned)(min(r, T - t0 - 1) * kstride + 8 * ((lane & 15) ^ (r & 15))), dst + 4096 * w + 1024 * i);
         }
+    };
+    auto issue_kq = [&](const ET *base, unsigned dst, int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue_kq_blk(base, dst, c, i);
     };
     auto issue_k = [&](int c) { issue_kq(kbase, L::oK + (c % 3) * L::KBUF, c); };
     auto issue_q = [&](int c) { issue_kq(qbase, L::oQ + (c & 1) * L::KBUF, c); };
@@ -252,8 +252,8 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 g2lds(src, 2 * (unsigned)(min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3)), dst + 1024 * i);
         }
     };
-    // g and beta of chunk c into LDS (prep wave 0; lane = token, rows past
-    // the end read the last row)
+    // g and beta of chunk c into LDS (wave 0 of a kind; lane = token, rows
+    // past the end read the last row)
     auto load_gb = [&](int c) {
         if (w == 0) {
             const int t0 = c * C;
@@ -270,7 +270,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma clang diagnostic pop
         }
     };
-    // Gate products of chunk c (prep wave 0, lane t holding g_t; g = 1 past
+    // Gate products of chunk c (wave 0 of a kind, lane t holding g_t; g = 1 past
     // the end): within each 16-token block (one DPP row) the inclusive prefix
     // products P and the inclusive suffix products by four doubling steps;
     // the exclusive suffix Sfx; block totals; G[t] = P[t] x totals of the
@@ -384,9 +384,13 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (state_wave) {
             // ================= state waves =================
             const unsigned lKt = f_lKt(), lKu = f_lKu(), lA = f_lA(), lVs = f_lVs();
-            // K of chunk n+2 and V of chunk n+1, both awaited before the phase
-            // barrier (V is read in phase b, K by the prep waves next chunk)
-            if (n + 2 < nchunks) issue_k(n + 2);
+            // K, g and beta of chunk n+2 and V of chunk n+1, all awaited before
+            // the phase barrier (V is read in phase b, K and the gate products
+            // by the prep waves next chunk)
+            if (n + 2 < nchunks) {
+                issue_k(n + 2);
+                load_gb(n + 2);
+            }
             if (n + 1 < nchunks) issue_v(n + 1);
             f32x4 D[NBT][NB], Y[NB][NBT];
             if (n >= 0) {
@@ -426,6 +430,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     for (int vb = 0; vb < NB; ++vb) Y[vb][tb] *= gt;
                 }
             }
+            if (n + 2 < nchunks) scan_gates(n + 2);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
             if (n >= 0) {
@@ -503,7 +508,6 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // ================= prep waves =================
             const int m = n + 1, p = w;
             const unsigned lKt = f_lKt(), lKtr = f_lKtr(), lWp = f_lWp(), lA = f_lA();
-            if (m + 1 < nchunks) load_gb(m + 1);
             if (m < nchunks) {
                 // ---- tiles of K K^T and Q K^T of chunk m; tile (jb, tb) has rows
                 // j = 16 jb + 4 qd + r and column t = 16 tb + x.  Prep wave p takes
@@ -622,7 +626,8 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
             lds_barrier();
-            // Q of chunk m + 1 (its buffer held Q of chunk m - 1, read in phase a)
+            // Q of chunk m + 1 (its buffer held Q of chunk m - 1, read in phase
+            // a), issued at once: its transfer then has the whole phase
             if (m + 1 < nchunks) issue_q(m + 1);
             if (m < nchunks) {
                 // ---- W of chunk m, key columns 32 p + 16 cb + x: RHS = beta G K
@@ -642,7 +647,6 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             *reinterpret_cast<ET *>(smem + L::oW + ((lWp ^ (rr << 4) ^ (64 * p + 32 * cb)) + 256 * rr + 4096 * ib)) = wv[rr];
                     });
             }
-            if (m + 1 < nchunks) scan_gates(m + 1);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         lds_barrier();
