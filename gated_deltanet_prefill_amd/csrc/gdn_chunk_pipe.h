@@ -32,7 +32,9 @@
 //             prep:  load Q_{n+2}; W_{n+1} (-W to LDS)
 //
 // U and W come from blocked forward substitution over 16-token blocks,
-//   X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j).
+//   X_i = T_ii diag(d) B_i + T_ii sum_{j<i} (-A_ij) X_j,
+// with B = V, d = beta for U and B = K, d = beta G for W: one 16x16x32
+// product per block, [T_ii diag(d) | T_ii] times [B_i ; Z_i].
 //
 // LDS layouts are swizzled so that the fragment reads and writes of each
 // buffer hit distinct banks: in the 256-byte rows of K, Q and -W (token rows,
@@ -50,6 +52,8 @@
 // so that the two tiles of a 32-key step give each lane eight consecutive
 // keys: the -W and Q operands of that step are then single 16-byte reads.
 #pragma once
+
+#include <type_traits>
 
 #include "gdn_chunk_impl.h"
 
@@ -76,10 +80,14 @@ struct PipeCfg {
     static constexpr unsigned oAn = oQKR + 2 * CBUF;     // -A [C][C]
     static constexpr unsigned LDD = 20;                  // floats per row of Ad
     static constexpr unsigned oAd = oAn + CBUF;          // A diagonal blocks [C][LDD] f32
-    static constexpr unsigned LDT = 24;                  // elements per row of Td
-    static constexpr unsigned oTd = oAd + C * LDD * 4;   // T diagonal blocks [C][LDT]
+    // Diagonal blocks of T with a scaled copy: row t holds, for q = 0..3,
+    // [T_ii diag(d) columns 4q..4q+3 | T_ii columns 4q..4q+3], d = beta G (TW,
+    // for W) or beta (TU, for U); 80-byte rows keep 16-byte reads conflict free.
+    static constexpr unsigned LDTT = 40;                 // elements per row of TW / TU
+    static constexpr unsigned oTW = oAd + C * LDD * 4;   // [C][LDTT]
+    static constexpr unsigned oTU = oTW + C * LDTT * 2;  // [C][LDTT]
     static constexpr unsigned NV = 7 * C;                // floats per gate-vector set
-    static constexpr unsigned oVec = oTd + C * LDT * 2;  // 3 x gate vectors
+    static constexpr unsigned oVec = oTU + C * LDTT * 2; // 3 x gate vectors
     static constexpr unsigned oGB = oVec + 3 * NV * 4;   // g, beta of the next chunk, as loaded
     static constexpr unsigned BYTES = oGB + 2 * C * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -312,16 +320,15 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     };
     static_assert(C == 64, "one lane per token in the gate scans");
 
-    // Blocked forward substitution for two 16-column tiles whose right-hand
-    // sides are rhs(ib, cb) (f32, lane x = column, rows 16 ib + 4 qd + r):
-    // X_i = T_ii (RHS_i + sum_{j<i} (-A_ij) X_j); emit(ib, cb, X_i f32).
-    // Returns the 16-bit blocks in Xf.
-    auto substitute = [&](unsigned lA, X4 (&Xf)[NBT][2], auto rhs, auto emit) {
+    // Blocked forward substitution for two 16-column tiles of
+    // X = T diag(d) B: bfrag(ib, cb) is the 16-bit fragment of B (lane x =
+    // column, rows 16 ib + 4 qd + r), tbuf holds [T_ii diag(d) | T_ii].
+    //   Z_i = sum_{j<i} (-A_ij) X_j,  X_i = [T_ii diag(d) | T_ii] [B_i ; Z_i];
+    // emit(ib, cb, X_i f32).  Returns the 16-bit blocks in Xf.
+    auto substitute = [&](unsigned lA, unsigned tbuf, X4 (&Xf)[NBT][2], auto bfrag, auto emit) {
 #pragma unroll
         for (int ib = 0; ib < NBT; ++ib) {
-            f32x4 Z[2];
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) Z[cb] = rhs(ib, cb);
+            f32x4 Z[2] = {zero4(), zero4()};
             // -A_ij X_j over j < ib, two blocks per 16x16x32 product; an odd
             // last block is paired with the diagonal block and a zero X.  Every
             // product into Z has the same shape: on gfx950 a 16x16x32 result
@@ -335,10 +342,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 for (int cb = 0; cb < 2; ++cb)
                     Z[cb] = mfma(fa, cat8<ET>(Xf[j][cb], j + 1 < ib ? Xf[j + 1][cb] : X4{}), Z[cb]);
             }
-            const X4 ft = lds4<ET>(smem, L::oTd + (16 * ib + x) * L::LDT * 2 + 8 * qd);
+            const X8 ft = lds8<ET>(smem, tbuf + (16 * ib + x) * L::LDTT * 2 + 16 * qd);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const f32x4 r = mfma(ft, cvt4<ET>(Z[cb]), zero4());
+                const f32x4 r = mfma(ft, cat8<ET>(bfrag(ib, cb), cvt4<ET>(Z[cb])), zero4());
                 Xf[ib][cb] = cvt4<ET>(r);
                 emit(ib, cb, r);
             }
@@ -488,16 +495,12 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
             if (n + 1 < nchunks) {
-                // ---- U of chunk n+1 for this wave's value columns: RHS = beta V,
-                // V read with the permuted columns of the value tiles.
-                const float *gv1 = Gv((n + 1) % 3);
+                // ---- U = T diag(beta) V of chunk n+1 for this wave's value
+                // columns, V read with the permuted columns of the value tiles.
                 const unsigned vsl = L::oV + w * L::VSL;
                 X4 Un[NBT][NB];
-                substitute(lA, Un,
-                    [&](int ib, int vb) {
-                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(gv1 + kVb * C + 16 * ib + 4 * qd);
-                        return to_f32x4<ET>(ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib)) * bv;
-                    },
+                substitute(lA, L::oTU, Un,
+                    [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib); },
                     [&](int, int, f32x4) {});
 #pragma unroll
                 for (int tb = 0; tb < NBT; ++tb)
@@ -511,15 +514,17 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             if (m < nchunks) {
                 // ---- tiles of K K^T and Q K^T of chunk m; tile (jb, tb) has rows
                 // j = 16 jb + 4 qd + r and column t = 16 tb + x.  Prep wave p takes
-                // the diagonal tiles of block p and three of the twelve below it:
-                //   wave 0: KK(0,1) QK(0,1) KK(0,2)   wave 1: QK(0,2) KK(1,2) QK(1,2)
-                //   wave 2: KK(0,3) QK(0,3) KK(1,3)   wave 3: QK(1,3) KK(2,3) QK(2,3)
+                // the diagonal tiles of block p and three of the twelve below it,
+                // chosen so that its own K_p (and Q_p) serve as operands:
+                //   wave 0: QK(0,2) KK(0,3) QK(0,3)   wave 1: KK(0,1) QK(0,1) QK(1,3)
+                //   wave 2: KK(1,2) QK(1,2) KK(0,2)   wave 3: KK(2,3) QK(2,3) KK(1,3)
+                // (4, 4, 4 and 5 fragment reads per 32-key step instead of 8).
                 const unsigned kbm = L::oK + (m % 3) * L::KBUF, qbm = L::oQ + (m & 1) * L::KBUF;
                 const unsigned rbm = L::oQKR + (m & 1) * L::CBUF;
                 const float *gv = Gv(m % 3);
                 // tile i of wave p: block row jb, block column tb, from Q or K,
                 // packed two bits per field at 6 p + 2 i (one bit at 3 p + i for Q)
-                constexpr unsigned kJB = 0xa50500u, kTB = 0xfffaa5u, kQB = 0xaaau;
+                constexpr unsigned kJB = 0x685400u, kTB = 0xfead7eu, kQB = 0x4b5u;
                 int tj[3], tt[3], tq[3];
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
@@ -530,19 +535,43 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 f32x4 acc[5];
 #pragma unroll
                 for (int i = 0; i < 5; ++i) acc[i] = zero4();
+                // acc[2 + i] = tile i: A operand K_jb, B operand K_tb or Q_tb
+                auto tiles = [&](auto P) {
+                    constexpr int pc = decltype(P)::value;
 #pragma unroll
-                for (int s = 0; s < NSK; ++s) {
-                    const unsigned lo = lKt ^ (64 * s);
-                    const X8 kp = lds8<ET>(smem, kbm + lo + 4096 * p);
-                    const X8 qp = lds8<ET>(smem, qbm + lo + 4096 * p);
-                    acc[0] = mfma(kp, kp, acc[0]);
-                    acc[1] = mfma(kp, qp, acc[1]);
-#pragma unroll
-                    for (int i = 0; i < 3; ++i) {
-                        const X8 fa = lds8<ET>(smem, kbm + lo + 4096 * tj[i]);
-                        const X8 fb = lds8<ET>(smem, (tq[i] ? qbm : kbm) + lo + 4096 * tt[i]);
-                        acc[2 + i] = mfma(fa, fb, acc[2 + i]);
+                    for (int s = 0; s < NSK; ++s) {
+                        const unsigned lo = lKt ^ (64 * s);
+                        const X8 kp = lds8<ET>(smem, kbm + lo + 4096 * pc);
+                        const X8 qp = lds8<ET>(smem, qbm + lo + 4096 * pc);
+                        acc[0] = mfma(kp, kp, acc[0]);
+                        acc[1] = mfma(kp, qp, acc[1]);
+                        if constexpr (pc == 0) {
+                            const X8 q2 = lds8<ET>(smem, qbm + lo + 4096 * 2);
+                            const X8 k3 = lds8<ET>(smem, kbm + lo + 4096 * 3);
+                            const X8 q3 = lds8<ET>(smem, qbm + lo + 4096 * 3);
+                            acc[2] = mfma(kp, q2, acc[2]);
+                            acc[3] = mfma(kp, k3, acc[3]);
+                            acc[4] = mfma(kp, q3, acc[4]);
+                        } else if constexpr (pc == 1) {
+                            const X8 k0 = lds8<ET>(smem, kbm + lo);
+                            const X8 q3 = lds8<ET>(smem, qbm + lo + 4096 * 3);
+                            acc[2] = mfma(k0, kp, acc[2]);
+                            acc[3] = mfma(k0, qp, acc[3]);
+                            acc[4] = mfma(kp, q3, acc[4]);
+                        } else {
+                            const X8 a1 = lds8<ET>(smem, kbm + lo + 4096 * (pc - 1));
+                            const X8 a2 = lds8<ET>(smem, kbm + lo + 4096 * (pc - 2));
+                            acc[2] = mfma(a1, kp, acc[2]);
+                            acc[3] = mfma(a1, qp, acc[3]);
+                            acc[4] = mfma(a2, kp, acc[4]);
+                        }
                     }
+                };
+                switch (p) {
+                case 0: tiles(std::integral_constant<int, 0>{}); break;
+                case 1: tiles(std::integral_constant<int, 1>{}); break;
+                case 2: tiles(std::integral_constant<int, 2>{}); break;
+                default: tiles(std::integral_constant<int, 3>{}); break;
                 }
                 // ---- diagonal block p: R[t][j] = g_{j+1} ... g_t inside the block;
                 // h = product of g over local indices [4 qd + 4, x] by an
@@ -620,9 +649,20 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         for (int mm = 0; mm < 4; ++mm)
                             if (4 * mm + 3 > j) sv[mm] -= arow[mm][j >> 2][j & 3] * xj;
                     }
-                    ET *td = reinterpret_cast<ET *>(smem + L::oTd);
+                    // column c of T_pp belongs to token 16 p + c: TW scales it by
+                    // beta G, TU by beta
+                    const float bc = gv[kVb * C + base + c], bgc = bc * gv[kVG * C + base + c];
+                    ET *tw = reinterpret_cast<ET *>(smem + L::oTW), *tu = reinterpret_cast<ET *>(smem + L::oTU);
+                    const int col = 8 * (c >> 2) + (c & 3);
 #pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) td[(base + pt + 4 * mm) * L::LDT + c] = from_f32<ET>(sv[mm]);
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const int o = (base + pt + 4 * mm) * L::LDTT + col;
+                        const ET tv = from_f32<ET>(sv[mm]);
+                        tw[o] = from_f32<ET>(sv[mm] * bgc);
+                        tw[o + 4] = tv;
+                        tu[o] = from_f32<ET>(sv[mm] * bc);
+                        tu[o + 4] = tv;
+                    }
                 }
             }
             lds_barrier();
@@ -630,16 +670,12 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // a), issued at once: its transfer then has the whole phase
             if (m + 1 < nchunks) issue_q(m + 1);
             if (m < nchunks) {
-                // ---- W of chunk m, key columns 32 p + 16 cb + x: RHS = beta G K
+                // ---- W = T diag(beta G) K of chunk m, key columns 32 p + 16 cb + x
                 const unsigned kbm = L::oK + (m % 3) * L::KBUF;
                 const float *gv = Gv(m % 3);
                 X4 Wf[NBT][2];
-                substitute(lA, Wf,
-                    [&](int ib, int cb) {
-                        const f32x4 bg = *reinterpret_cast<const f32x4 *>(gv + kVb * C + 16 * ib + 4 * qd) *
-                                         *reinterpret_cast<const f32x4 *>(gv + kVG * C + 16 * ib + 4 * qd);
-                        return to_f32x4<ET>(ld_tr<ET>(smem, kbm + (lKtr ^ (32 * (2 * p + cb))) + 4096 * ib)) * bg;
-                    },
+                substitute(lA, L::oTW, Wf,
+                    [&](int ib, int cb) { return ld_tr<ET>(smem, kbm + (lKtr ^ (32 * (2 * p + cb))) + 4096 * ib); },
                     [&](int ib, int cb, f32x4 r) {
                         const X4 wv = cvt4<ET>(-r);
 #pragma unroll
