@@ -400,6 +400,19 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
             if (n + 1 < nchunks) issue_v(n + 1);
             f32x4 D[NBT][NB], Y[NB][NBT];
+            // ---- U = T diag(beta) V of chunk n+1 for this wave's value columns,
+            // V read with the permuted columns of the value tiles
+            auto compute_u = [&]() {
+                const unsigned vsl = L::oV + w * L::VSL;
+                X4 Un[NBT][NB];
+                substitute(lA, L::oTU, Un,
+                    [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib); },
+                    [&](int, int, f32x4) {});
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Uf[tb][vb] = Un[tb][vb];
+            };
             if (n >= 0) {
                 // ---- phase a: D = U + (-W) S^T, Y^T = S Q^T
                 const unsigned qb = L::oQ + (n & 1) * L::KBUF;
@@ -461,13 +474,20 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             Y[vb][tb] = mfma(cat8<ET>(Df[2 * s][vb], Df[2 * s + 1][vb]), fr, Y[vb][tb]);
                     }
                 }
-                // y: lane (x, qd) holds token 16 tb + x, values 32 w + 8 qd + (0..7)
-                ET *yc = y + (((size_t)b * T + t0) * Hv + hv) * DV + 32 * w + 8 * qd;
+                // y: lane (x, qd) holds token 16 tb + x, values 32 w + 8 qd + (0..7).
+                // The stores go through a buffer resource that spans the chunk's
+                // cn valid token rows: the hardware drops those past the end of
+                // the sequence, with no branch around the stores.
+                {
+                    typedef int i32x4 __attribute__((ext_vector_type(4)));
+                    const unsigned rowb = (unsigned)(Hv * DV) * (unsigned)sizeof(ET);
+                    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(y + (((size_t)b * T + t0) * Hv + hv) * DV), (short)0, (int)(cn * rowb), 0x00020000);
 #pragma unroll
-                for (int tb = 0; tb < NBT; ++tb) {
-                    const int t = 16 * tb + x;
-                    if (t < cn)
-                        *reinterpret_cast<X8 *>(yc + (size_t)t * Hv * DV) = cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]));
+                    for (int tb = 0; tb < NBT; ++tb)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(i32x4, cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]))), yr,
+                            (int)((16 * tb + x) * rowb + (32 * w + 8 * qd) * sizeof(ET)), 0, 0);
                 }
                 X4 Dp[NBT][NB];
 #pragma unroll
@@ -493,19 +513,12 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         for (int vb = 0; vb < NB; ++vb)
                             S[kb][vb] = mfma(fk[s], cat8<ET>(Dp[2 * s][vb], Dp[2 * s + 1][vb]), S[kb][vb]);
                 }
-            }
-            if (n + 1 < nchunks) {
-                // ---- U = T diag(beta) V of chunk n+1 for this wave's value
-                // columns, V read with the permuted columns of the value tiles.
-                const unsigned vsl = L::oV + w * L::VSL;
-                X4 Un[NBT][NB];
-                substitute(lA, L::oTU, Un,
-                    [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib); },
-                    [&](int, int, f32x4) {});
-#pragma unroll
-                for (int tb = 0; tb < NBT; ++tb)
-#pragma unroll
-                    for (int vb = 0; vb < NB; ++vb) Uf[tb][vb] = Un[tb][vb];
+                // in the same block as the work above, so that the scheduler can
+                // interleave the chains (after the last chunk it reads stale LDS
+                // and its result is not used)
+                compute_u();
+            } else {
+                compute_u();
             }
         } else {
             // ================= prep waves =================
