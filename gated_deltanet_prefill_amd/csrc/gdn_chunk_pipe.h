@@ -360,6 +360,16 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
     auto kcol = [&](int kb, int q4) { return 32 * (kb >> 1) + 8 * q4 + 4 * (kb & 1); };
 
+    // QKR blocks above the diagonal are never written: zero both buffers once.
+    auto zero_qkr = [&]() {
+        for (int i = tid; i < (int)(2 * L::CBUF / 16); i += 512)
+            reinterpret_cast<uint4 *>(smem + L::oQKR)[i] = zero_u4();
+    };
+
+    // The two kinds of waves run loops of their own with the same barriers
+    // (two per chunk), so that each loop carries only its own registers; the
+    // first chunk step of the state waves and the last of the prep waves,
+    // which do only part of the work, are taken out of the loops.
     if (state_wave) {
         if (nchunks > 0) {
             issue_k(0);
@@ -376,44 +386,49 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else if (nchunks > 0) {
-        // gates of chunk 0 (its V comes in the first iteration)
-        load_gb(0);
-        scan_gates(0);
-    }
-    // QKR blocks above the diagonal are never written: zero both buffers once.
-    for (int i = tid; i < (int)(2 * L::CBUF / 16); i += 512)
-        reinterpret_cast<uint4 *>(smem + L::oQKR)[i] = zero_u4();
-    lds_barrier();
-
-    for (int n = -1; n < nchunks; ++n) {
-        asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
-        if (state_wave) {
-            // ================= state waves =================
-            const unsigned lKt = f_lKt(), lKu = f_lKu(), lA = f_lA(), lVs = f_lVs();
-            // K, g and beta of chunk n+2 and V of chunk n+1, all awaited before
-            // the phase barrier (V is read in phase b, K and the gate products
-            // by the prep waves next chunk)
+        zero_qkr();
+        lds_barrier();
+        // K, g and beta of chunk n+2 and V of chunk n+1, all awaited before the
+        // phase-a barrier (V is read in phase b, K and the gate products by the
+        // prep waves next chunk)
+        auto issue_inputs = [&](int n) {
             if (n + 2 < nchunks) {
                 issue_k(n + 2);
                 load_gb(n + 2);
             }
             if (n + 1 < nchunks) issue_v(n + 1);
+        };
+        auto end_phase_a = [&](int n) {
+            if (n + 2 < nchunks) scan_gates(n + 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+        };
+        // ---- U = T diag(beta) V of chunk n+1 for this wave's value columns,
+        // V read with the permuted columns of the value tiles (after the last
+        // chunk this reads stale LDS; its result is not used)
+        auto compute_u = [&]() {
+            const unsigned lA = f_lA(), vsl = L::oV + w * L::VSL + f_lVs();
+            X4 Un[NBT][NB];
+            substitute(lA, L::oTU, Un,
+                [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + 8 * vb + 1024 * ib); },
+                [&](int, int, f32x4) {});
+#pragma unroll
+            for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) Uf[tb][vb] = Un[tb][vb];
+        };
+        // chunk step -1: inputs of chunks 0 (V) and 1 (K, gates), U of chunk 0
+        issue_inputs(-1);
+        end_phase_a(-1);
+        compute_u();
+        lds_barrier();
+        for (int n = 0; n < nchunks; ++n) {
+            asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
+            // ================= state waves =================
+            const unsigned lKt = f_lKt(), lKu = f_lKu(), lA = f_lA();
+            issue_inputs(n);
             f32x4 D[NBT][NB], Y[NB][NBT];
-            // ---- U = T diag(beta) V of chunk n+1 for this wave's value columns,
-            // V read with the permuted columns of the value tiles
-            auto compute_u = [&]() {
-                const unsigned vsl = L::oV + w * L::VSL;
-                X4 Un[NBT][NB];
-                substitute(lA, L::oTU, Un,
-                    [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + lVs + 8 * vb + 1024 * ib); },
-                    [&](int, int, f32x4) {});
-#pragma unroll
-                for (int tb = 0; tb < NBT; ++tb)
-#pragma unroll
-                    for (int vb = 0; vb < NB; ++vb) Uf[tb][vb] = Un[tb][vb];
-            };
-            if (n >= 0) {
+            {
                 // ---- phase a: D = U + (-W) S^T, Y^T = S Q^T
                 const unsigned qb = L::oQ + (n & 1) * L::KBUF;
                 const float *gv = Gv(n % 3);
@@ -450,10 +465,8 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     for (int vb = 0; vb < NB; ++vb) Y[vb][tb] *= gt;
                 }
             }
-            if (n + 2 < nchunks) scan_gates(n + 2);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
-            if (n >= 0) {
+            end_phase_a(n);
+            {
                 // ---- phase b: Y^T += D^T QKR^T, y, S^T <- G_last S^T + K^T diag(Rl) D
                 const int t0 = n * C, cn = min(C, T - t0);
                 const unsigned kb_ = L::oK + (n % 3) * L::KBUF, rb_ = L::oQKR + (n & 1) * L::CBUF;
@@ -514,17 +527,33 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             S[kb][vb] = mfma(fk[s], cat8<ET>(Dp[2 * s][vb], Dp[2 * s + 1][vb]), S[kb][vb]);
                 }
                 // in the same block as the work above, so that the scheduler can
-                // interleave the chains (after the last chunk it reads stale LDS
-                // and its result is not used)
-                compute_u();
-            } else {
+                // interleave the chains
                 compute_u();
             }
-        } else {
+            lds_barrier();
+        }
+        // ---- the state, written once
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb)
+                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd)) = S[kb][vb];
+    } else {
+        if (nchunks > 0) {
+            // gates of chunk 0 (its V comes in the first iteration)
+            load_gb(0);
+            scan_gates(0);
+        }
+        zero_qkr();
+        lds_barrier();
+        // chunk m = n + 1 of every step but the last, which only keeps the two
+        // barriers of the state waves' last chunk
+        for (int n = -1; n + 1 < nchunks; ++n) {
+            asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
             // ================= prep waves =================
             const int m = n + 1, p = w;
             const unsigned lKt = f_lKt(), lKtr = f_lKtr(), lWp = f_lWp(), lA = f_lA();
-            if (m < nchunks) {
+            {
                 // ---- tiles of K K^T and Q K^T of chunk m; tile (jb, tb) has rows
                 // j = 16 jb + 4 qd + r and column t = 16 tb + x.  Prep wave p takes
                 // the diagonal tiles of block p and three of the twelve below it,
@@ -682,7 +711,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // Q of chunk m + 1 (its buffer held Q of chunk m - 1, read in phase
             // a), issued at once: its transfer then has the whole phase
             if (m + 1 < nchunks) issue_q(m + 1);
-            if (m < nchunks) {
+            {
                 // ---- W = T diag(beta G) K of chunk m, key columns 32 p + 16 cb + x
                 const unsigned kbm = L::oK + (m % 3) * L::KBUF;
                 const float *gv = Gv(m % 3);
@@ -697,17 +726,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     });
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
         }
         lds_barrier();
-    }
-
-    // ---- the state, written once
-    if (state_wave) {
-#pragma unroll
-        for (int vb = 0; vb < NB; ++vb)
-#pragma unroll
-            for (int kb = 0; kb < NBK; ++kb)
-                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd)) = S[kb][vb];
+        lds_barrier();
     }
 }
 
