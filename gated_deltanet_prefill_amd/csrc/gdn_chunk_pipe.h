@@ -175,9 +175,9 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int r4 = 4 * qd + (x >> 2);
         return (unsigned)(r4 * 256 + ((((x & 3) ^ r4) & 15) << 4));
     };
-    // -W, prep side: element (t = 16 ib + 4 qd + r, key 32 p + 16 cb + x), 2
-    // bytes: (this ^ (r << 4) ^ (64 p + 32 cb)) + 256 r + 4096 ib
-    auto f_lWp = [&]() { return (unsigned)(4 * qd * 256 + ((((x >> 3) ^ (4 * qd)) & 15) << 4) + 2 * (x & 7)); };
+    // -W, prep side: token 16 ib + x, keys 16 c + 4 qd .. + 3 (8 bytes) of
+    // key tile c: ^ 32 c, + 4096 ib
+    auto f_lWp = [&]() { return (unsigned)(x * 256 + ((((qd >> 1) ^ x) & 15) << 4) + 8 * (qd & 1)); };
     // QKR / -A rows 16 tb + x, the 4 columns 16 jb + 4 qd ..:
     //   (this ^ 64 (jb/2)) + 8 (jb%2) + 2048 tb;
     // the 8 columns of blocks 2 s, 2 s + 1 that lane (x, qd) holds: ^ 64 s
@@ -324,7 +324,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // X = T diag(d) B: bfrag(ib, cb) is the 16-bit fragment of B (lane x =
     // column, rows 16 ib + 4 qd + r), tbuf holds [T_ii diag(d) | T_ii].
     //   Z_i = sum_{j<i} (-A_ij) X_j,  X_i = [T_ii diag(d) | T_ii] [B_i ; Z_i];
-    // emit(ib, cb, X_i f32).  Returns the 16-bit blocks in Xf.
+    // emit(ib, cb, X_i f32, the two operands).  Returns the 16-bit blocks in Xf.
     auto substitute = [&](unsigned lA, unsigned tbuf, X4 (&Xf)[NBT][2], auto bfrag, auto emit) {
 #pragma unroll
         for (int ib = 0; ib < NBT; ++ib) {
@@ -345,9 +345,10 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             const X8 ft = lds8<ET>(smem, tbuf + (16 * ib + x) * L::LDTT * 2 + 16 * qd);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const f32x4 r = mfma(ft, cat8<ET>(bfrag(ib, cb), cvt4<ET>(Z[cb])), zero4());
+                const X8 bz = cat8<ET>(bfrag(ib, cb), cvt4<ET>(Z[cb]));
+                const f32x4 r = mfma(ft, bz, zero4());
                 Xf[ib][cb] = cvt4<ET>(r);
-                emit(ib, cb, r);
+                emit(ib, cb, r, ft, bz);
             }
         }
     };
@@ -411,7 +412,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             X4 Un[NBT][NB];
             substitute(lA, L::oTU, Un,
                 [&](int ib, int vb) { return ld_tr<ET>(smem, vsl + 8 * vb + 1024 * ib); },
-                [&](int, int, f32x4) {});
+                [&](int, int, f32x4, X8, X8) {});
 #pragma unroll
             for (int tb = 0; tb < NBT; ++tb)
 #pragma unroll
@@ -718,11 +719,11 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 X4 Wf[NBT][2];
                 substitute(lA, L::oTW, Wf,
                     [&](int ib, int cb) { return ld_tr<ET>(smem, kbm + (lKtr ^ (32 * (2 * p + cb))) + 4096 * ib); },
-                    [&](int ib, int cb, f32x4 r) {
-                        const X4 wv = cvt4<ET>(-r);
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr)
-                            *reinterpret_cast<ET *>(smem + L::oW + ((lWp ^ (rr << 4) ^ (64 * p + 32 * cb)) + 256 * rr + 4096 * ib)) = wv[rr];
+                    // the same product with the operands swapped gives the block
+                    // transposed, lane (x, qd) holding keys 4 qd .. + 3 of token
+                    // 16 ib + x: one 8-byte write into the token rows of -W
+                    [&](int ib, int cb, f32x4, X8 ft, X8 bz) {
+                        sts4<ET>(smem, L::oW + (lWp ^ (32 * (2 * p + cb))) + 4096 * ib, cvt4<ET>(-mfma(bz, ft, zero4())));
                     });
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
