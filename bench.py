@@ -21,6 +21,10 @@ printed with:
 * ``decode``      256 chained ``gdn_step`` launches on the decode workload
                   (B=64, Hk=16, Hv=32, Dk=Dv=128, fp16 I/O, f32 state in
                   place): state GB/s and total GB/s against 8 TB/s;
+* ``multi_token`` T = 2, 4, 8 tokens per call on the decode shapes: the
+                  sequential kernel (``gdn_seq_fwd``), the chunked kernel at
+                  C = 16 and the library's own choice (C = 0), each call
+                  timed alone with the state coming from HBM;
 * ``cpu_baseline`` the float64 CPU oracle timed on a bounded sample of the
                   same workload (4 of the 8 batch elements: all heads, all
                   8192 tokens), with the thread count it used.
@@ -176,6 +180,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args()
@@ -346,6 +351,55 @@ def main():
             },
         }
         del toks, ys, st, st0, dq, dk, dv, dg, db
+
+    # ---------------- a few tokens per call (speculative or batched decode)
+    if not args.no_multi:
+        D = DECODE
+        dinp = gi.workload_inputs("decode")
+        st0 = upload(dinp["state"], "f32")
+        scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        rows = []
+        for T in (2, 4, 8):
+            tq, tk, tv = (upload(dinp[n][:, :T], "f16") for n in ("q", "k", "v"))
+            tg, tb = upload(dinp["g"][:, :T], "f32"), upload(dinp["beta"][:, :T], "f32")
+            ty = torch.empty((D["B"], T, D["Hv"], D["Dv"]), dtype=torch.float16, device=dev)
+            sa, sb = st0.clone(), torch.empty_like(st0)
+            calls = {"seq": lambda a, b: gdn.seq_fwd(tq, tk, tv, tg, tb, a, state_out=b, y=ty,
+                                                     stream=stream),
+                     "chunk16": lambda a, b: gdn.chunk_fwd(tq, tk, tv, tg, tb, a, C=16, state_out=b,
+                                                           y=ty, stream=stream),
+                     "auto": lambda a, b: gdn.chunk_fwd(tq, tk, tv, tg, tb, a, C=0, state_out=b,
+                                                        y=ty, stream=stream)}
+            row = {"T": T}
+            for name, call in calls.items():
+                n = 16
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(n + 1)]
+                for i in range(n + 1):               # the first call warms up
+                    scratch.sum()
+                    evs[i][0].record(stream)
+                    call(sa, sb)
+                    evs[i][1].record(stream)
+                    sa, sb = sb, sa
+                torch.cuda.synchronize()
+                row[f"{name}_us"] = sum(a.elapsed_time(b) for a, b in evs[1:]) * 1e3 / n
+            sbytes, tbytes = step_bytes(**D)
+            ibytes = (tbytes - sbytes) * T             # per-token inputs and outputs
+            best = min(row[f"{n}_us"] for n in calls)
+            row["tokens_per_s"] = D["B"] * T / (row["auto_us"] * 1e-6)
+            row["hbm_frac_auto"] = (sbytes + ibytes) / (row["auto_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+            row["auto_vs_best"] = row["auto_us"] / best
+            rows.append(row)
+            del tq, tk, tv, tg, tb, ty, sa, sb
+        del scratch, st0
+        out["multi_token"] = {
+            "workload": "decode shapes, T tokens per call", "B": D["B"], "Hk": D["Hk"],
+            "Hv": D["Hv"], "Dk": D["Dk"], "Dv": D["Dv"], "dtype": "f16",
+            "rows": rows,
+            "method": "state ping-pongs between two buffers; 512 MiB scratch read between "
+                      "calls; each call timed alone with HIP events; 16 calls per entry",
+            "hbm_bytes": "state read + write once per call plus q, k, v, y, g, beta of T tokens",
+        }
 
     # ---------------- CPU oracle on a bounded sample
     if not args.no_cpu_baseline:

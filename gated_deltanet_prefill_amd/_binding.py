@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
 SUPPORTED_DIMS = (32, 64, 128)
-SUPPORTED_CHUNKS = (16, 32, 64)
+SUPPORTED_CHUNKS = (0, 16, 32, 64)     # 0: the library chooses
 
 _lib = None
 
@@ -41,6 +41,8 @@ def load() -> ctypes.CDLL:
         vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
         lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 8 + [vp]
         lib.gdn_chunk_fwd.restype = i
+        lib.gdn_seq_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [vp]
+        lib.gdn_seq_fwd.restype = i
         lib.gdn_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 6 + [vp]
         lib.gdn_step.restype = i
         lib.gdn_status_string.argtypes = [i]
@@ -75,15 +77,7 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def chunk_fwd(q, k, v, g, beta, state_in=None, *, C=64, state_out=None, y=None,
-              stream=None):
-    """``gdn_chunk_fwd`` on torch tensors.  Returns ``(y, state_out)``.
-
-    q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv] (float32, bfloat16 or float16); g, beta
-    [B,T,Hv] float32; state_in [B,Hv,Dv,Dk] float32 or None.  Outputs are
-    allocated when not given; ``state_out`` may be ``state_in`` (in place).
-    """
-    lib = load()
+def _prefill_args(q, k, v, g, beta, state_in, state_out, y):
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dev, dt = q.device, q.dtype
@@ -102,6 +96,33 @@ def chunk_fwd(q, k, v, g, beta, state_in=None, *, C=64, state_out=None, y=None,
     if y is None:
         y = torch.empty((B, T, Hv, Dv), dtype=dt, device=dev)
     _check_tensor("y", y, (B, T, Hv, Dv), dt, dev)
+    return (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y
+
+
+def seq_fwd(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None):
+    """``gdn_seq_fwd`` on torch tensors (token by token, the state read once).
+    Arguments and result as for :func:`chunk_fwd` (without ``C``)."""
+    lib = load()
+    (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
+    rc = lib.gdn_seq_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                         _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv,
+                         DTYPE_CODE[dt], _stream_handle(stream, dev))
+    if rc != 0:
+        raise GDNError("gdn_seq_fwd", rc, status_string(rc))
+    return y, state_out
+
+
+def chunk_fwd(q, k, v, g, beta, state_in=None, *, C=64, state_out=None, y=None,
+              stream=None):
+    """``gdn_chunk_fwd`` on torch tensors.  Returns ``(y, state_out)``.
+
+    q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv] (float32, bfloat16 or float16); g, beta
+    [B,T,Hv] float32; state_in [B,Hv,Dv,Dk] float32 or None.  Outputs are
+    allocated when not given; ``state_out`` may be ``state_in`` (in place).
+    ``C = 0`` lets the library choose the kernel and the chunk length.
+    """
+    lib = load()
+    (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
     rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                            _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, int(C),
                            DTYPE_CODE[dt], _stream_handle(stream, dev))

@@ -68,6 +68,39 @@ int check(const void *q, const void *k, const void *v, const float *g,
     return GDN_OK;
 }
 
+// The automatic choice of gdn_chunk_fwd (C = 0), from launch timings on the
+// MI355X.  The sequential kernel costs one read and one write of the state
+// plus a few microseconds per token at the largest grids; the chunked kernel
+// has a higher fixed cost and a far smaller one per token, so the sequential
+// kernel wins up to a handful of tokens (more for float32 inputs, whose
+// chunked kernel runs its products at the float32 MFMA rate).
+bool seq_for(int dtype, int T) { return T <= (dtype == GDN_F32 ? 12 : 6); }
+
+// Chunk length: 16 keeps the most work in flight per token and wins on
+// grids of many (batch, head) slots; the pipelined 64-token kernel (16-bit
+// inputs, 128-dimensional heads) wins once each slot has enough chunks to
+// fill its pipeline, which takes more tokens the more slots share the chip.
+// For other 16-bit head sizes 32 wins from about 64 tokens; for float32
+// inputs 16 is never more than a few percent off.
+int chunk_for(int dtype, int Dk, int Dv, long slots, int T) {
+    if (dtype != GDN_F32 && Dk == 128 && Dv == 128) {
+        if (T >= 48 && 16L * T >= 3L * slots) return 64;
+        if (T >= 16 && slots <= 256) return 32;
+    } else if (dtype != GDN_F32 && T >= 64) {
+        return 32;
+    }
+    return 16;
+}
+
+int launch(const gdn::FwdArgs &a, int dtype, bool seq, hipStream_t stream) {
+    hipError_t e;
+    if (seq) e = gdn::launch_seq(dtype, a, stream);
+    else if (dtype == GDN_F32) e = gdn::launch_chunk_f32(a, stream);
+    else if (dtype == GDN_BF16) e = gdn::launch_chunk_bf16(a, stream);
+    else e = gdn::launch_chunk_f16(a, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,17 +113,27 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
 {
     int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
     if (rc != GDN_OK) return rc;
-    if (C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
+    if (C != 0 && C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
+    const bool seq = C == 0 && seq_for((int)dtype, T);
+    if (C == 0) C = chunk_for((int)dtype, Dk, Dv, (long)B * Hv, T);
     gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
                    B, T, Hk, Hv, Dk, Dv, C, (float)(1.0 / sqrt((double)Dk))};
-    hipError_t e;
-    switch (dtype) {
-    case GDN_F32: e = gdn::launch_chunk_f32(a, stream); break;
-    case GDN_BF16: e = gdn::launch_chunk_bf16(a, stream); break;
-    default: e = gdn::launch_chunk_f16(a, stream); break;
-    }
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launch(a, (int)dtype, seq, stream);
+}
+
+int gdn_seq_fwd(const void *q, const void *k, const void *v,
+                const float *g, const float *beta,
+                const float *state_in, float *state_out, void *y,
+                int B, int T, int Hk, int Hv, int Dk, int Dv,
+                gdn_dtype dtype, hipStream_t stream)
+{
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    if (rc != GDN_OK) return rc;
+    if (B == 0) return GDN_OK;
+    gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
+                   B, T, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk))};
+    return launch(a, (int)dtype, true, stream);
 }
 
 int gdn_step(const void *q, const void *k, const void *v,
@@ -114,7 +157,7 @@ const char *gdn_status_string(int status)
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "a required pointer is NULL";
     case GDN_ERR_SHAPE: return "invalid shape (negative size, or Hv not a multiple of Hk)";
-    case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be 32, 64 or 128; C must be 16, 32 or 64)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be 32, 64 or 128; C must be 0, 16, 32 or 64)";
     case GDN_ERR_ALIAS: return "an output overlaps another buffer";
     case GDN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, y, state; 4 for g, beta)";
     case GDN_ERR_HIP: return "HIP launch failed";
@@ -123,6 +166,6 @@ const char *gdn_status_string(int status)
     }
 }
 
-int gdn_version(void) { return 100; }
+int gdn_version(void) { return 10100; }
 
 }  // extern "C"

@@ -20,6 +20,7 @@ hipError_t launch_chunk_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_f16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_step(int dtype, const FwdArgs &a, hipStream_t s);
+hipError_t launch_seq(int dtype, const FwdArgs &a, hipStream_t s);
 
 // Largest chunk the float32 path can hold in LDS; bigger requests run with
 // this chunk length (the result does not depend on the chunk length).

@@ -84,7 +84,10 @@ enum {
  *   Hk, Hv      key and value heads, Hv % Hk == 0.
  *   Dk, Dv      head dimensions, each one of 32, 64, 128.
  *   C           chunk length, one of 16, 32, 64 (the tail chunk of
- *               T - C*floor(T/C) tokens is handled inside the kernel).
+ *               T - C*floor(T/C) tokens is handled inside the kernel), or 0:
+ *               let the library choose, for this shape and T, between the
+ *               sequential kernel of gdn_seq_fwd (short T) and the chunked
+ *               kernel with a chunk length of its own choice.
  *   dtype       storage type of q, k, v, y.
  *   stream      HIP stream (NULL = default stream).
  * Returns GDN_OK or a GDN_ERR_* code.
@@ -94,6 +97,26 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *state_in, float *state_out, void *y,
                   int B, int T, int Hk, int Hv, int Dk, int Dv, int C,
                   gdn_dtype dtype, hipStream_t stream);
+
+/*
+ * gdn_seq_fwd -- T tokens of the rule, token by token, with the state read
+ * once from state_in and written once to state_out: the sequential rule
+ * itself (the ferrox-core gdn_chunk.rs page, "The algebra", takes it as the
+ * definition the chunked form must match), each state row held in registers
+ * across the tokens.  Faster than gdn_chunk_fwd for short T (a few tokens of
+ * decode or speculation), where the chunk's triangular solve does not pay.
+ *   The gates are applied through a running per-slot scale that is folded
+ *   into the state when it leaves [2^-24, 2^24]; results equal those of T
+ *   calls of gdn_step up to float32 rounding.
+ *   Arguments, layouts, alignment, aliasing and errors as for gdn_chunk_fwd
+ *   (without C); Dk and Dv each one of 32, 64, 128; T = 0 copies the initial
+ *   state (or zeros) to state_out.
+ */
+int gdn_seq_fwd(const void *q, const void *k, const void *v,
+                const float *g, const float *beta,
+                const float *state_in, float *state_out, void *y,
+                int B, int T, int Hk, int Hv, int Dk, int Dv,
+                gdn_dtype dtype, hipStream_t stream);
 
 /*
  * gdn_step -- one token of the rule (decode): each state row is read once

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gdn_chunk_fwd", "gdn_step", "gdn_status_string", "gdn_version"} <= set(names)
+    assert {"gdn_chunk_fwd", "gdn_seq_fwd", "gdn_step", "gdn_status_string", "gdn_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
 
@@ -54,6 +54,12 @@ def chunk(lib, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=6 * A, so=7 * A, y=8 
                              B, T, Hk, Hv, Dk, Dv, C, dtype, None)
 
 
+def seq(lib, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=6 * A, so=7 * A, y=8 * A,
+        B=1, T=4, Hk=1, Hv=1, Dk=32, Dv=32, dtype=1):
+    return lib.gdn_seq_fwd(P(q), P(k), P(v), P(g), P(b), P(si), P(so), P(y),
+                           B, T, Hk, Hv, Dk, Dv, dtype, None)
+
+
 def step(lib, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=6 * A, so=7 * A, y=8 * A,
          B=1, Hk=1, Hv=1, Dk=32, Dv=32, dtype=1):
     return lib.gdn_step(P(q), P(k), P(v), P(g), P(b), P(si), P(so), P(y),
@@ -66,6 +72,8 @@ def test_shape_errors(lib):
     assert chunk(lib, Hk=0) == SHAPE
     assert chunk(lib, Hk=2, Hv=3) == SHAPE
     assert step(lib, Hk=3, Hv=4) == SHAPE
+    assert seq(lib, T=-1) == SHAPE
+    assert seq(lib, Hk=2, Hv=3) == SHAPE
 
 
 def test_unsupported(lib):
@@ -73,12 +81,15 @@ def test_unsupported(lib):
     assert chunk(lib, Dv=256) == UNSUP
     assert chunk(lib, C=8) == UNSUP
     assert chunk(lib, C=128) == UNSUP
+    assert chunk(lib, C=-16) == UNSUP
+    assert seq(lib, Dv=96) == UNSUP
     assert step(lib, Dk=16) == UNSUP
 
 
 def test_dtype(lib):
     assert chunk(lib, dtype=3) == DTYPE
     assert step(lib, dtype=-1) == DTYPE
+    assert seq(lib, dtype=7) == DTYPE
 
 
 def test_null(lib):
@@ -86,6 +97,8 @@ def test_null(lib):
     for name in ("q", "k", "v", "g", "b", "y"):
         assert chunk(lib, **{name: 0}) == NULL, name
     assert step(lib, q=0) == NULL
+    assert seq(lib, so=0) == NULL
+    assert seq(lib, k=0) == NULL
 
 
 def test_alignment(lib):
@@ -93,6 +106,7 @@ def test_alignment(lib):
     assert chunk(lib, so=7 * A + 4) == ALIGN
     assert chunk(lib, g=4 * A + 2) == ALIGN
     assert step(lib, y=8 * A + 2) == ALIGN
+    assert seq(lib, v=3 * A + 4) == ALIGN
 
 
 def test_aliasing(lib):
@@ -105,9 +119,12 @@ def test_aliasing(lib):
     # y overlapping state_out
     assert chunk(lib, y=7 * A + 64) == ALIAS
     assert step(lib, y=2 * A) == ALIAS
+    assert seq(lib, so=5 * A) == ALIAS
 
 
 def test_empty_batch_is_a_no_op(lib):
     # B = 0: nothing to do, and no pointer is needed
     assert chunk(lib, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
     assert step(lib, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
+    assert seq(lib, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
+    assert chunk(lib, B=0, C=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK

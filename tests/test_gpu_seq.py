@@ -1,0 +1,162 @@
+"""GPU parity of gdn_seq_fwd (the token-by-token prefill kernel) and of
+gdn_chunk_fwd with C = 0 (the library picks the kernel) against the f64
+oracle, through the C ABI.
+
+Covers short and ragged lengths (T = 0 included), every dtype and head size,
+grouped heads, the absent and the in-place state, the decode workload's 256
+tokens on sampled slots, agreement with the chunked kernel, and a long
+sequence in one call (error growth over many recurrent steps).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gdn_testlib import assert_parity, oracle_run, to_host_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_seq(gdn, inp, state=True, **kw):
+    d = upload(inp, state=state)
+    y, s = gdn.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], **kw)
+    torch.cuda.synchronize()
+    return to_host_f64(y), to_host_f64(s)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_seq_lengths(gpu_lib, dtype):
+    for T in (1, 2, 7, 16, 33):
+        inp = gi.make_inputs(2, T, 2, 4, 128, 128, dtype, gate="sigmoid", state_std=0.3, seed=70 + T)
+        y, s = run_seq(gpu_lib, inp)
+        yr, sr = oracle_run(inp)
+        assert_parity(y, s, yr, sr, dtype, f"seq {dtype} T={T}")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (128, 32), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_seq_head_dims(gpu_lib, dk, dv, dtype):
+    inp = gi.make_inputs(2, 9, 1, 3, dk, dv, dtype, gate="softplus", state_std=0.1, seed=dk + 3 * dv)
+    y, s = run_seq(gpu_lib, inp)
+    yr, sr = oracle_run(inp)
+    assert_parity(y, s, yr, sr, dtype, f"seq {dtype} Dk={dk} Dv={dv}")
+
+
+@pytest.mark.parametrize("hk,hv", [(1, 1), (1, 4), (2, 6), (16, 32)])
+def test_seq_grouped_heads(gpu_lib, hk, hv):
+    inp = gi.make_inputs(3, 6, hk, hv, 128, 128, "bf16", gate="sigmoid", state_std=0.1, seed=hk * 7 + hv)
+    y, s = run_seq(gpu_lib, inp)
+    yr, sr = oracle_run(inp)
+    assert_parity(y, s, yr, sr, "bf16", f"seq Hk={hk} Hv={hv}")
+
+
+@pytest.mark.parametrize("B,hv,dv,dtype", [(8, 32, 128, "bf16"), (16, 32, 128, "f32"), (16, 32, 64, "f16")])
+def test_seq_rows_per_lane(gpu_lib, B, hv, dv, dtype):
+    """Grids large enough for two and four value rows per lane (the kernel
+    packs more rows per lane when the grid has waves to spare)."""
+    inp = gi.make_inputs(B, 3, 16, hv, 128, dv, dtype, gate="sigmoid", state_std=0.2, seed=B + dv)
+    y, s = run_seq(gpu_lib, inp)
+    yr, sr = oracle_run(inp)
+    assert_parity(y, s, yr, sr, dtype, f"seq B={B} Hv={hv} Dv={dv}")
+
+
+def test_seq_gate_extremes(gpu_lib):
+    """Zero, tiny and unit gates, and a run of small ones whose product
+    leaves the float range: the kernel's deferred decay must fold and
+    restart without loss."""
+    inp = gi.make_inputs(2, 40, 1, 2, 64, 64, "f32", gate="sigmoid", state_std=0.3, seed=41)
+    g = inp["g"]
+    g[:, 0:3] = 1.0
+    g[:, 3] = 0.0
+    g[:, 4:9] = 1e-20
+    g[:, 9:30] = 0.05
+    g[0, 35] = 0.0
+    y, s = run_seq(gpu_lib, inp)
+    yr, sr = oracle_run(inp)
+    assert_parity(y, s, yr, sr, "f32", "seq gate extremes")
+
+
+def test_seq_null_and_in_place_state(gpu_lib):
+    inp = gi.make_inputs(2, 5, 2, 4, 128, 128, "f16", gate="sigmoid", state_std=0.2, seed=11)
+    y, s = run_seq(gpu_lib, inp, state=False)
+    yr, sr = oracle_run(inp, state=False)
+    assert_parity(y, s, yr, sr, "f16", "seq null state")
+    d = upload(inp)
+    st = d["state"].clone()
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    yr, sr = oracle_run(inp)
+    assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, "f16", "seq in-place state")
+
+
+def test_seq_empty(gpu_lib):
+    inp = gi.make_inputs(2, 0, 1, 2, 64, 64, "bf16", state_std=0.1, seed=1)
+    d = upload(inp)
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 2, 64)
+    assert torch.equal(s, d["state"])
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(s) == 0
+
+
+def test_seq_decode_tokens_sampled(gpu_lib):
+    """The decode workload's 256 tokens in one call, checked on six slots."""
+    inp = gi.workload_inputs("decode")
+    d = upload(inp)
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    torch.cuda.synchronize()
+    B, Hv = 64, 32
+    mask = np.zeros((B, Hv), bool)
+    for b, hv in [(0, 0), (2, 3), (19, 7), (40, 16), (51, 29), (63, 31)]:
+        mask[b, hv] = True
+    yr, sr = oracle_run(inp, slot_mask=mask)
+    yg, sg = to_host_f64(y), to_host_f64(s)
+    assert_parity(yg, sg, yr, sr, "f16", "seq over decode tokens (6 slots)",
+                  np.broadcast_to(mask[:, None, :, None], yg.shape),
+                  np.broadcast_to(mask[:, :, None, None], sg.shape))
+    assert np.isfinite(yg).all() and np.isfinite(sg).all()
+
+
+def test_seq_matches_chunk_and_step(gpu_lib):
+    """Three kernels, one recurrence: seq, chunk and chained steps agree."""
+    inp = gi.make_inputs(2, 24, 2, 4, 128, 128, "f32", gate="sigmoid", state_std=0.2, seed=21)
+    d = upload(inp)
+    ys, ss = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    yc, sc = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=16)
+    st = d["state"].clone()
+    ysteps = []
+    for t in range(24):
+        y, st = gpu_lib.step(*(d[n][:, t].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                             st, state_out=st)
+        ysteps.append(y)
+    torch.cuda.synchronize()
+    yt = torch.stack(ysteps, 1)
+    # seq and step run the same per-token arithmetic; chunk reorders it
+    assert torch.allclose(ys, yt, rtol=1e-5, atol=1e-6) and torch.allclose(ss, st, rtol=1e-5, atol=1e-6)
+    yr, sr = oracle_run(inp)
+    for y, s, what in ((ys, ss, "seq"), (yc, sc, "chunk C=16"), (yt, st, "steps")):
+        assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, "f32", what)
+
+
+def test_seq_long_sequence(gpu_lib):
+    """600 recurrent steps in one call (state error compounds over steps)."""
+    inp = gi.make_inputs(1, 600, 1, 2, 128, 128, "bf16", gate="softplus", state_std=0.1, seed=31)
+    y, s = run_seq(gpu_lib, inp)
+    yr, sr = oracle_run(inp)
+    assert_parity(y, s, yr, sr, "bf16", "seq T=600")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_auto_chunk(gpu_lib, dtype):
+    """C = 0: the library's own choice of kernel and chunk length is right
+    on both sides of the switch from token-by-token to chunked."""
+    for T in (1, 3, 8, 15, 16, 17, 40, 100, 300):
+        inp = gi.make_inputs(2, T, 2, 4, 128, 128, dtype, gate="sigmoid", state_std=0.2, seed=500 + T)
+        d = upload(inp)
+        y, s = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=0)
+        torch.cuda.synchronize()
+        yr, sr = oracle_run(inp)
+        assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, dtype, f"auto {dtype} T={T}")
