@@ -50,7 +50,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.gdn_ref_forward.argtypes = [dp] * 8 + [ctypes.c_long] * 6 + [
-            ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         lib.gdn_ref_forward.restype = ctypes.c_int
         lib.gdn_ref_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -71,15 +71,34 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def forward(q, k, v, g, beta, state=None, *, slot_mask=None, nthreads=0):
+HEAD_MAPS = ("grouped", "tiled")
+GATES = ("decay", "log")
+
+
+def key_heads(Hk: int, Hv: int, head_map: str = "grouped") -> np.ndarray:
+    """Key head of every value head: ``hv // (Hv // Hk)`` (grouped, the
+    metaltile-std page's "Layouts") or ``hv % Hk`` (tiled, the other map the
+    ferrox-core page's host body selects)."""
+    if head_map not in HEAD_MAPS:
+        raise ValueError(f"head_map must be one of {HEAD_MAPS}")
+    hv = np.arange(Hv)
+    return hv % Hk if head_map == "tiled" else hv // (Hv // Hk)
+
+
+def forward(q, k, v, g, beta, state=None, *, slot_mask=None, nthreads=0,
+            head_map="grouped", gate="decay"):
     """Sequential rule in C, float64.
 
     ``q, k`` [B,T,Hk,Dk], ``v`` [B,T,Hv,Dv], ``g, beta`` [B,T,Hv] and
     ``state`` [B,Hv,Dv,Dk] (or None for a zero initial state) are float64
     arrays (use :func:`gdn_inputs.decode` on stored inputs).  Returns
     ``(y, state_out)`` in float64.  ``slot_mask`` (bool [B,Hv]) restricts
-    the work to some slots; the others come back as NaN.
+    the work to some slots; the others come back as NaN.  ``head_map``
+    picks the key head of each value head (:func:`key_heads`); ``gate`` says
+    whether ``g`` is the decay or its natural logarithm.
     """
+    if head_map not in HEAD_MAPS or gate not in GATES:
+        raise ValueError("head_map / gate")
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -96,26 +115,29 @@ def forward(q, k, v, g, beta, state=None, *, slot_mask=None, nthreads=0):
         mask = np.ascontiguousarray(np.asarray(slot_mask, dtype=np.uint8).reshape(B * Hv))
     rc = _load().gdn_ref_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s_in), _ptr(s_out),
-        _ptr(y), B, T, Hk, Hv, Dk, Dv,
+        _ptr(y), B, T, Hk, Hv, Dk, Dv, HEAD_MAPS.index(head_map), GATES.index(gate),
         None if mask is None else mask.ctypes.data_as(ctypes.c_void_p), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"gdn_ref_forward failed ({rc})")
     return y, s_out
 
 
-def forward_numpy(q, k, v, g, beta, state=None):
+def forward_numpy(q, k, v, g, beta, state=None, *, head_map="grouped", gate="decay"):
     """Sequential rule in NumPy, float64 (tiny cases).
 
     Same contract as :func:`forward`.  Token loop; every slot advances at
-    once: the value head ``hv`` reads key head ``hv // (Hv // Hk)`` (the
-    grouped map of the metaltile-std page, "Layouts").
+    once: the value head ``hv`` reads key head ``key_heads(...)[hv]``.
     """
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     if Hv % Hk:
         raise ValueError("Hv must be a multiple of Hk")
-    head_of = np.arange(Hv) // (Hv // Hk)
+    head_of = key_heads(Hk, Hv, head_map)
+    if gate not in GATES:
+        raise ValueError("gate")
+    if gate == "log":
+        g = np.exp(g)
     S = np.zeros((B, Hv, Dv, Dk)) if state is None else _f64(state).copy()
     y = np.empty((B, T, Hv, Dv))
     scale = 1.0 / np.sqrt(Dk)

@@ -18,7 +18,13 @@
  * Layouts as on the metaltile-std gated_delta_wy.rs page ("Layouts"):
  * q,k [B,T,Hk,Dk]; v,y [B,T,Hv,Dv]; g,beta [B,T,Hv]; state [B,Hv,Dv,Dk],
  * state row j (value index) holding Dk contiguous key-index entries.
- * Grouped query heads as on that page: hk = hv / (Hv / Hk).
+ * Key head of value head hv: grouped as on that page, hk = hv / (Hv / Hk)
+ * (head_map 0), or tiled, hk = hv mod Hk (head_map 1): the two head maps
+ * the ferrox-core page's host body chooses between when it picks the key
+ * head of a value head.
+ * Gate input: the decay itself (log_gate 0), or its natural logarithm
+ * (log_gate 1), which the ferrox-core page's host body turns into the decay
+ * with exp before use.
  *
  * Everything is float64 with plain loops in token order.  Slots (b, hv) are
  * independent (ferrox-core page: "Heads are independent") and run on an
@@ -40,10 +46,12 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
                     const double *g, const double *beta,
                     const double *state_in, double *state_out, double *y,
                     long B, long T, long Hk, long Hv, long Dk, long Dv,
+                    int head_map, int log_gate,
                     const unsigned char *slot_mask, int nthreads)
 {
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0) return -1;
     if (Hv % Hk != 0) return -1;
+    if ((head_map != 0 && head_map != 1) || (log_gate != 0 && log_gate != 1)) return -1;
     if (!state_out) return -1;
     if (T > 0 && (!q || !k || !v || !g || !beta || !y)) return -1;
     const long group = Hv / Hk;
@@ -56,7 +64,8 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
 #endif
     for (long slot = 0; slot < nslots; ++slot) {
         if (slot_mask && !slot_mask[slot]) continue;
-        const long b = slot / Hv, hv = slot % Hv, hk = hv / group;
+        const long b = slot / Hv, hv = slot % Hv;
+        const long hk = head_map == 1 ? hv % Hk : hv / group;
         double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk));
         double *pred = (double *)malloc(sizeof(double) * (size_t)Dv);
         if (!S || !pred) {
@@ -73,7 +82,8 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
             const double *kt = k + ((b * T + t) * Hk + hk) * Dk;
             const double *qt = q + ((b * T + t) * Hk + hk) * Dk;
             const double *vt = v + ((b * T + t) * Hv + hv) * Dv;
-            const double gt = g[(b * T + t) * Hv + hv];
+            const double gin = g[(b * T + t) * Hv + hv];
+            const double gt = log_gate ? exp(gin) : gin;
             const double bt = beta[(b * T + t) * Hv + hv];
             double *yt = y + ((b * T + t) * Hv + hv) * Dv;
             /* prediction from the decayed previous state: g_t S_{t-1} k_t */

@@ -42,12 +42,14 @@ def upload(inp, device="cuda", state=True):
     return d
 
 
-def oracle_run(inp, slot_mask=None, state=True):
+def oracle_run(inp, slot_mask=None, state=True, head_map="grouped", gate="decay"):
+    """The oracle on stored inputs; with ``gate="log"`` the stored ``g`` is
+    taken as the logarithm of the decay."""
     dt = inp["dtype"]
     q, k, v = (gi.decode(inp[n], dt) for n in ("q", "k", "v"))
     s = inp["state"].astype(np.float64) if (state and inp["state"] is not None) else None
     return oracle.forward(q, k, v, inp["g"].astype(np.float64), inp["beta"].astype(np.float64),
-                          s, slot_mask=slot_mask)
+                          s, slot_mask=slot_mask, head_map=head_map, gate=gate)
 
 
 def gap(got: np.ndarray, ref: np.ndarray, mask=None) -> float:

@@ -304,3 +304,95 @@ def test_c_slot_mask_and_empty():
     # T = 0: the state passes through
     y0, s0 = oracle.forward(q[:, :0], k[:, :0], v[:, :0], g[:, :0], beta[:, :0], S0)
     assert y0.shape == (2, 0, 2, 3) and np.array_equal(s0, S0)
+
+
+# ------------------------------------------- head maps and the log gate
+# The ferrox-core page's host body selects the key head of a value head
+# through one of two head maps, "Tiled" or "Grouped", and takes the gate as
+# the logarithm of the decay (it applies exp before use).  The grouped map is
+# pinned above; the tiled map is pinned to it through the cases where the two
+# coincide and through a relabelling of the value heads.
+
+def _tiled_to_grouped_perm(Hk, Hv):
+    """Position p[hv] that value head hv takes so that the grouped map of
+    position p[hv] is the key head the tiled reading gives hv (hv mod Hk):
+    the value heads of key head h are listed together, in head order."""
+    grp = Hv // Hk
+    return np.array([(hv % Hk) * grp + hv // Hk for hv in range(Hv)])
+
+
+def check_tiled_heads(fwd):
+    rng = np.random.default_rng(31)
+    ok = True
+    # Hk == Hv and Hk == 1: the two maps agree
+    for Hk, Hv in ((3, 3), (1, 4)):
+        q, k, v, g, beta, S0 = rand_case(rng, B=2, T=5, Hk=Hk, Hv=Hv, Dk=4, Dv=3)
+        yt, st = fwd(q, k, v, g, beta, S0, head_map="tiled")
+        yg, sg = fwd(q, k, v, g, beta, S0, head_map="grouped")
+        ok &= np.allclose(yt, yg, rtol=0, atol=1e-14) and np.allclose(st, sg, rtol=0, atol=1e-14)
+    # Hk = 2, Hv = 6: tiled == grouped after moving value head hv to p[hv]
+    Hk, Hv = 2, 6
+    q, k, v, g, beta, S0 = rand_case(rng, B=2, T=6, Hk=Hk, Hv=Hv, Dk=4, Dv=3)
+    p = _tiled_to_grouped_perm(Hk, Hv)
+    assert sorted(p) == list(range(Hv))
+    vp, gp, bp, sp = (np.empty_like(a) for a in (v, g, beta, S0))
+    vp[:, :, p], gp[:, :, p], bp[:, :, p], sp[:, p] = v, g, beta, S0
+    yt, st = fwd(q, k, v, g, beta, S0, head_map="tiled")
+    yg, sg = fwd(q, k, vp, gp, bp, sp, head_map="grouped")
+    ok &= np.allclose(yt, yg[:, :, p], rtol=0, atol=1e-13) and np.allclose(st, sg[:, p], rtol=0, atol=1e-13)
+    # and the maps really differ there
+    yg0, _ = fwd(q, k, v, g, beta, S0, head_map="grouped")
+    ok &= not np.allclose(yt, yg0, atol=1e-6)
+    return bool(ok)
+
+
+def check_log_gate(fwd):
+    rng = np.random.default_rng(32)
+    q, k, v, g, beta, S0 = rand_case(rng, B=1, T=6, Hk=1, Hv=2, Dk=4, Dv=3)
+    ok = True
+    # a log gate of log(g) is the decay g
+    yl, sl = fwd(q, k, v, np.log(g), beta, S0, gate="log")
+    yd, sd = fwd(q, k, v, g, beta, S0, gate="decay")
+    ok &= np.allclose(yl, yd, rtol=1e-13, atol=1e-14) and np.allclose(sl, sd, rtol=1e-13, atol=1e-14)
+    # log gate 0 is decay 1 (no forgetting), exactly
+    yl, sl = fwd(q, k, v, np.zeros_like(g), beta, S0, gate="log")
+    yd, sd = fwd(q, k, v, np.ones_like(g), beta, S0, gate="decay")
+    ok &= np.array_equal(yl, yd) and np.array_equal(sl, sd)
+    # log gate -inf is decay 0: y_t = b_t v_t (k_t . q_t) / sqrt(Dk)
+    yl, sl = fwd(q, k, v, np.full_like(g, -np.inf), beta, S0, gate="log")
+    kq = np.einsum("td,td->t", k[0, :, 0], q[0, :, 0])
+    want = beta[0, :, :, None] * v[0] * kq[:, None, None] / 2.0
+    ok &= np.allclose(yl[0], want, rtol=0, atol=1e-14)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("name", list(ORACLES))
+@pytest.mark.parametrize("check", [check_tiled_heads, check_log_gate], ids=lambda c: c.__name__)
+def test_oracle_options(name, check):
+    assert check(ORACLES[name])
+
+
+def _option_mutant(kind):
+    """The NumPy oracle with a planted mistake in one option."""
+    def fwd(q, k, v, g, beta, state=None, *, head_map="grouped", gate="decay"):
+        if gate == "log":
+            g = {"log_negated": lambda x: np.exp(-x), "log_ignored": lambda x: x}.get(kind, np.exp)(g)
+        if head_map == "tiled" and kind == "tiled_as_block":
+            head_map = "grouped"
+        if head_map == "tiled" and kind == "tiled_wrong_index":
+            # value head hv reads key head (hv // Hk) mod Hk: give every value
+            # head its own copy of that key head and map them one to one
+            Hk, Hv = q.shape[2], v.shape[2]
+            sel = (np.arange(Hv) // Hk) % Hk
+            return oracle.forward_numpy(q[:, :, sel], k[:, :, sel], v, g, beta, state)
+        return oracle.forward_numpy(q, k, v, g, beta, state, head_map=head_map)
+    return fwd
+
+
+@pytest.mark.parametrize("kind,check", [("tiled_as_block", check_tiled_heads),
+                                        ("tiled_wrong_index", check_tiled_heads),
+                                        ("log_negated", check_log_gate),
+                                        ("log_ignored", check_log_gate)])
+def test_option_mistake_is_caught(kind, check):
+    with np.errstate(all="ignore"):
+        assert not check(_option_mutant(kind))
