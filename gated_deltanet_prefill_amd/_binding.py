@@ -18,6 +18,9 @@ GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
 SUPPORTED_DIMS = (32, 64, 128)
 SUPPORTED_CHUNKS = (0, 16, 32, 64)     # 0: the library chooses
+GDN_HEADS_TILED, GDN_GATE_LOG = 1, 2
+HEAD_MAPS = ("grouped", "tiled")
+GATES = ("decay", "log")
 
 _lib = None
 
@@ -45,6 +48,12 @@ def load() -> ctypes.CDLL:
         lib.gdn_seq_fwd.restype = i
         lib.gdn_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 6 + [vp]
         lib.gdn_step.restype = i
+        lib.gdn_chunk_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 9 + [vp]
+        lib.gdn_chunk_fwd_ex.restype = i
+        lib.gdn_seq_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 8 + [vp]
+        lib.gdn_seq_fwd_ex.restype = i
+        lib.gdn_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [vp]
+        lib.gdn_step_ex.restype = i
         lib.gdn_status_string.argtypes = [i]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_version.restype = i
@@ -77,6 +86,14 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _flags(heads, gate):
+    if heads not in HEAD_MAPS:
+        raise ValueError(f"heads must be one of {HEAD_MAPS}")
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {GATES}")
+    return (GDN_HEADS_TILED if heads == "tiled" else 0) | (GDN_GATE_LOG if gate == "log" else 0)
+
+
 def _prefill_args(q, k, v, g, beta, state_in, state_out, y):
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -99,45 +116,54 @@ def _prefill_args(q, k, v, g, beta, state_in, state_out, y):
     return (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y
 
 
-def seq_fwd(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None):
-    """``gdn_seq_fwd`` on torch tensors (token by token, the state read once).
-    Arguments and result as for :func:`chunk_fwd` (without ``C``)."""
+def seq_fwd(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None,
+            heads="grouped", gate="decay"):
+    """``gdn_seq_fwd_ex`` on torch tensors (token by token, the state read
+    once).  Arguments and result as for :func:`chunk_fwd` (without ``C``)."""
     lib = load()
+    flags = _flags(heads, gate)
     (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
-    rc = lib.gdn_seq_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                         _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv,
-                         DTYPE_CODE[dt], _stream_handle(stream, dev))
+    rc = lib.gdn_seq_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                            _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, flags,
+                            DTYPE_CODE[dt], _stream_handle(stream, dev))
     if rc != 0:
-        raise GDNError("gdn_seq_fwd", rc, status_string(rc))
+        raise GDNError("gdn_seq_fwd_ex", rc, status_string(rc))
     return y, state_out
 
 
 def chunk_fwd(q, k, v, g, beta, state_in=None, *, C=64, state_out=None, y=None,
-              stream=None):
+              stream=None, heads="grouped", gate="decay"):
     """``gdn_chunk_fwd`` on torch tensors.  Returns ``(y, state_out)``.
 
     q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv] (float32, bfloat16 or float16); g, beta
     [B,T,Hv] float32; state_in [B,Hv,Dv,Dk] float32 or None.  Outputs are
     allocated when not given; ``state_out`` may be ``state_in`` (in place).
     ``C = 0`` lets the library choose the kernel and the chunk length.
+    ``heads`` is the head map ("grouped": key head hv // (Hv // Hk);
+    "tiled": hv % Hk) and ``gate`` says whether ``g`` is the decay or its
+    natural logarithm ("decay" / "log").
     """
     lib = load()
+    flags = _flags(heads, gate)
     (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
-    rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                           _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, int(C),
-                           DTYPE_CODE[dt], _stream_handle(stream, dev))
+    rc = lib.gdn_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                              _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, int(C), flags,
+                              DTYPE_CODE[dt], _stream_handle(stream, dev))
     if rc != 0:
-        raise GDNError("gdn_chunk_fwd", rc, status_string(rc))
+        raise GDNError("gdn_chunk_fwd_ex", rc, status_string(rc))
     return y, state_out
 
 
-def step(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None):
-    """``gdn_step`` on torch tensors (one token).  Returns ``(y, state_out)``.
+def step(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None,
+         heads="grouped", gate="decay"):
+    """``gdn_step_ex`` on torch tensors (one token).  Returns ``(y, state_out)``.
 
     q, k [B,Hk,Dk]; v [B,Hv,Dv]; g, beta [B,Hv] float32; state_in
     [B,Hv,Dv,Dk] float32 or None; ``state_out`` may be ``state_in``.
+    ``heads`` and ``gate`` as for :func:`chunk_fwd`.
     """
     lib = load()
+    flags = _flags(heads, gate)
     B, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     dev, dt = q.device, q.dtype
@@ -156,9 +182,9 @@ def step(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None
     if y is None:
         y = torch.empty((B, Hv, Dv), dtype=dt, device=dev)
     _check_tensor("y", y, (B, Hv, Dv), dt, dev)
-    rc = lib.gdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                      _ptr(state_out), _ptr(y), B, Hk, Hv, Dk, Dv, DTYPE_CODE[dt],
-                      _stream_handle(stream, dev))
+    rc = lib.gdn_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                         _ptr(state_out), _ptr(y), B, Hk, Hv, Dk, Dv, flags, DTYPE_CODE[dt],
+                         _stream_handle(stream, dev))
     if rc != 0:
-        raise GDNError("gdn_step", rc, status_string(rc))
+        raise GDNError("gdn_step_ex", rc, status_string(rc))
     return y, state_out

@@ -12,6 +12,10 @@
 
 namespace {
 
+static_assert(GDN_HEADS_TILED == gdn::kTiledHeads && GDN_GATE_LOG == gdn::kLogGate,
+              "flag values of the ABI and the kernels");
+constexpr int kKnownFlags = GDN_HEADS_TILED | GDN_GATE_LOG;
+
 struct Range {
     uintptr_t lo, hi;                 // [lo, hi); empty when lo == hi
 };
@@ -105,21 +109,47 @@ int launch(const gdn::FwdArgs &a, int dtype, bool seq, hipStream_t stream) {
 
 extern "C" {
 
+int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                     const float *g, const float *beta,
+                     const float *state_in, float *state_out, void *y,
+                     int B, int T, int Hk, int Hv, int Dk, int Dv, int C, int flags,
+                     gdn_dtype dtype, hipStream_t stream)
+{
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    if (rc != GDN_OK) return rc;
+    if (C != 0 && C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    const bool seq = C == 0 && seq_for((int)dtype, T);
+    if (C == 0) C = chunk_for((int)dtype, Dk, Dv, (long)B * Hv, T);
+    gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
+                   B, T, Hk, Hv, Dk, Dv, C, (float)(1.0 / sqrt((double)Dk)), flags};
+    return launch(a, (int)dtype, seq, stream);
+}
+
 int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *g, const float *beta,
                   const float *state_in, float *state_out, void *y,
                   int B, int T, int Hk, int Hv, int Dk, int Dv, int C,
                   gdn_dtype dtype, hipStream_t stream)
 {
+    return gdn_chunk_fwd_ex(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, C,
+                            0, dtype, stream);
+}
+
+int gdn_seq_fwd_ex(const void *q, const void *k, const void *v,
+                   const float *g, const float *beta,
+                   const float *state_in, float *state_out, void *y,
+                   int B, int T, int Hk, int Hv, int Dk, int Dv, int flags,
+                   gdn_dtype dtype, hipStream_t stream)
+{
     int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
     if (rc != GDN_OK) return rc;
-    if (C != 0 && C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
-    const bool seq = C == 0 && seq_for((int)dtype, T);
-    if (C == 0) C = chunk_for((int)dtype, Dk, Dv, (long)B * Hv, T);
     gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
-                   B, T, Hk, Hv, Dk, Dv, C, (float)(1.0 / sqrt((double)Dk))};
-    return launch(a, (int)dtype, seq, stream);
+                   B, T, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk)), flags};
+    return launch(a, (int)dtype, true, stream);
 }
 
 int gdn_seq_fwd(const void *q, const void *k, const void *v,
@@ -128,12 +158,24 @@ int gdn_seq_fwd(const void *q, const void *k, const void *v,
                 int B, int T, int Hk, int Hv, int Dk, int Dv,
                 gdn_dtype dtype, hipStream_t stream)
 {
-    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    return gdn_seq_fwd_ex(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, 0,
+                          dtype, stream);
+}
+
+int gdn_step_ex(const void *q, const void *k, const void *v,
+                const float *g, const float *beta,
+                const float *state_in, float *state_out, void *y,
+                int B, int Hk, int Hv, int Dk, int Dv, int flags,
+                gdn_dtype dtype, hipStream_t stream)
+{
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, 1, Hk, Hv, Dk, Dv, (int)dtype);
     if (rc != GDN_OK) return rc;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
     gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
-                   B, T, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk))};
-    return launch(a, (int)dtype, true, stream);
+                   B, 1, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk)), flags};
+    hipError_t e = gdn::launch_step((int)dtype, a, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_step(const void *q, const void *k, const void *v,
@@ -142,13 +184,8 @@ int gdn_step(const void *q, const void *k, const void *v,
              int B, int Hk, int Hv, int Dk, int Dv,
              gdn_dtype dtype, hipStream_t stream)
 {
-    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, 1, Hk, Hv, Dk, Dv, (int)dtype);
-    if (rc != GDN_OK) return rc;
-    if (B == 0) return GDN_OK;
-    gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
-                   B, 1, Hk, Hv, Dk, Dv, 0, (float)(1.0 / sqrt((double)Dk))};
-    hipError_t e = gdn::launch_step((int)dtype, a, stream);
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return gdn_step_ex(q, k, v, g, beta, state_in, state_out, y, B, Hk, Hv, Dk, Dv, 0, dtype,
+                       stream);
 }
 
 const char *gdn_status_string(int status)
@@ -157,7 +194,7 @@ const char *gdn_status_string(int status)
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "a required pointer is NULL";
     case GDN_ERR_SHAPE: return "invalid shape (negative size, or Hv not a multiple of Hk)";
-    case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be 32, 64 or 128; C must be 0, 16, 32 or 64)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size or flag (Dk, Dv must be 32, 64 or 128; C must be 0, 16, 32 or 64; flags only GDN_HEADS_TILED | GDN_GATE_LOG)";
     case GDN_ERR_ALIAS: return "an output overlaps another buffer";
     case GDN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, y, state; 4 for g, beta)";
     case GDN_ERR_HIP: return "HIP launch failed";
@@ -166,6 +203,6 @@ const char *gdn_status_string(int status)
     }
 }
 
-int gdn_version(void) { return 10100; }
+int gdn_version(void) { return 10200; }
 
 }  // extern "C"

@@ -17,7 +17,7 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((chunk_pipe_kernel<ET, DK, DV, C>), dim3((unsigned)nslots), dim3(512), 0, st,
                            static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                            static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale);
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale, a.flags);
         return hipGetLastError();
     } else {
         // 32 value columns per wave for Dv = 128, else 16 (more waves, fewer
@@ -32,7 +32,8 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), grid, block, 0, st,
                            static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                            static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale);
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale,
+                           a.flags);
         return hipGetLastError();
     }
 }

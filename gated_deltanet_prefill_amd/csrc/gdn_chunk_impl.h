@@ -187,7 +187,8 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                       const ET *__restrict__ v, const float *__restrict__ g,
                       const float *__restrict__ beta, const float *state_in,
                       float *state_out, ET *__restrict__ y,
-                      int T, int Hk, int Hv, int Dv, int nsplit, int xcd_group, float scale)
+                      int T, int Hk, int Hv, int Dv, int nsplit, int xcd_group, float scale,
+                      int flags)
 {
     using L = ChunkCfg<ET, DK, DVS, C, NB>;
     using X4 = typename Vec<ET>::x4;
@@ -227,8 +228,10 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int sib = kk % xcd_group, m = kk / xcd_group;
         bid = (m * 8 + xcd) * xcd_group + sib;
     }
-    const int slot = bid / nsplit, vs = bid - slot * nsplit;
-    const int hv = slot % Hv, b = slot / Hv, hk = hv / (Hv / Hk);
+    const int rank = bid / nsplit, vs = bid - rank * nsplit;
+    const int b = rank / Hv, hv = value_head_of_rank(rank % Hv, Hk, Hv, flags);
+    const int hk = key_head(hv, Hk, Hv, flags);
+    const int slot = b * Hv + hv;
     const int vloc = wave * 16 * NB;               // first slice column of this wave
 
     // ---- the state, S^T tiles [key block][value block], f32 accumulators
@@ -332,7 +335,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // doubling steps; block totals BT; G[t] = P[t] * BT of earlier
         // blocks; Rl[t] = R[c-1][t] = Sfx[t] * BT of later blocks.
         if (wave == 0) {
-            const float gt = (tid < cn) ? rg : 1.f;
+            const float gt = (tid < cn) ? decay_of(rg, flags) : 1.f;
             float p = gt, sx = gt;
             p *= dpp_row_shr<1>(p);
             p *= dpp_row_shr<2>(p);

@@ -127,7 +127,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                        const ET *__restrict__ v, const float *__restrict__ g,
                        const float *__restrict__ beta, const float *state_in,
                        float *state_out, ET *__restrict__ y,
-                       int T, int Hk, int Hv, int xcd_group, float scale)
+                       int T, int Hk, int Hv, int xcd_group, float scale, int flags)
 {
     using L = PipeCfg<ET, DK, DV, C>;
     using X4 = typename Vec<ET>::x4;
@@ -150,14 +150,16 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // Workgroups are dealt round-robin over the 8 XCDs, so workgroups i and
     // i + 8 share an XCD and its L2; with xcd_group = Hv/Hk > 1 they get
     // value heads of the same key head, whose q/k stream is then fetched
-    // from HBM once per group.
+    // from HBM once per group.  bid counts slots with the value heads of one
+    // key head adjacent, under either head map.
     int bid = blockIdx.x;
     if (xcd_group > 1) {
         const int xcd = bid & 7, kk = bid >> 3;
         const int sib = kk % xcd_group, mm = kk / xcd_group;
         bid = (mm * 8 + xcd) * xcd_group + sib;
     }
-    const int hv = bid % Hv, b = bid / Hv, hk = hv / (Hv / Hk);
+    const int b = bid / Hv, hv = value_head_of_rank(bid % Hv, Hk, Hv, flags);
+    const int hk = key_head(hv, Hk, Hv, flags);
     const int nchunks = (T + C - 1) / C;
 
     // ---- lane-dependent LDS byte offsets (see the layout notes above)
@@ -290,7 +292,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             const float rb = reinterpret_cast<const float *>(smem + L::oGB)[C + lane];
             const int cn = min(C, T - c * C);
             float *gv = Gv(c % 3);
-            const float gt = lane < cn ? rg : 1.f;
+            const float gt = lane < cn ? decay_of(rg, flags) : 1.f;
             float p = gt, sx = gt;
             p *= dpp_row_shr<1>(p);
             p *= dpp_row_shr<2>(p);
@@ -357,7 +359,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // S[kb][vb]: S^T tile, rows = keys kcol(kb, qd) + r, columns = values.
     f32x4 S[NBK][NB];
     X4 Uf[NBT][NB];                              // U of the next chunk (own value columns)
-    const size_t sbase = (size_t)bid * DV * DK;
+    const size_t sbase = ((size_t)b * Hv + hv) * DV * DK;
     auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
     auto kcol = [&](int kb, int q4) { return 32 * (kb >> 1) + 8 * q4 + 4 * (kb & 1); };
 

@@ -18,6 +18,7 @@
 // their fragments with one 8-byte (16-bit types) or 16-byte (f32) read.
 #pragma once
 
+#include "gdn_internal.h"
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,6 +29,26 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// The decay a gate input stands for: the value itself, or exp of it when
+// the caller passes log-decays (the ferrox-core gdn_chunk.rs page's host
+// body takes the gate in that form and exponentiates it).
+__device__ __forceinline__ float decay_of(float g, int flags) {
+    return (flags & kLogGate) ? expf(g) : g;
+}
+
+// Key head read by value head hv: grouped (hv / (Hv / Hk), the layout of the
+// metaltile-std gated_delta_wy.rs page) or tiled (hv mod Hk).
+__device__ __forceinline__ int key_head(int hv, int Hk, int Hv, int flags) {
+    return (flags & kTiledHeads) ? hv % Hk : hv / (Hv / Hk);
+}
+
+// Value head of the r-th slot of a batch element when slots are counted with
+// the value heads of each key head adjacent (key head r / (Hv / Hk)).
+__device__ __forceinline__ int value_head_of_rank(int r, int Hk, int Hv, int flags) {
+    const int group = Hv / Hk;
+    return (flags & kTiledHeads) ? (r % group) * Hk + r / group : r;
+}
 
 template <typename T> struct Vec;
 template <> struct Vec<float> { using x4 = f32x4; };

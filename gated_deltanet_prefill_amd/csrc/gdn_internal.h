@@ -5,6 +5,11 @@
 
 namespace gdn {
 
+// Bits of FwdArgs::flags (the GDN_HEADS_TILED and GDN_GATE_LOG values of
+// the C ABI).
+constexpr int kTiledHeads = 1;     // key head of value head hv is hv mod Hk
+constexpr int kLogGate = 2;        // g holds log(decay)
+
 struct FwdArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -13,6 +18,7 @@ struct FwdArgs {
     void *y;
     int B, T, Hk, Hv, Dk, Dv, C;
     float scale;
+    int flags = 0;
 };
 
 // Each returns hipSuccess or the launch error; arguments are already valid.

@@ -28,7 +28,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                  const ET *__restrict__ v, const float *__restrict__ g,
                  const float *__restrict__ beta, const float *state_in,
                  float *state_out, ET *__restrict__ y,
-                 int Hk, int Hv, int Dv, float scale)
+                 int Hk, int Hv, int Dv, float scale, int flags)
 {
     constexpr int LPR = kStepLanesPerRow;
     constexpr int NP = DK / (4 * LPR);            // 16-byte state pieces per lane
@@ -37,7 +37,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const int blocks_per_slot = Dv / kStepRowsPerBlock;
     const int slot = blockIdx.x / blocks_per_slot;
     const int j = (blockIdx.x - slot * blocks_per_slot) * kStepRowsPerBlock + tid / LPR;
-    const int hv = slot % Hv, b = slot / Hv, hk = hv / (Hv / Hk);
+    const int hv = slot % Hv, b = slot / Hv, hk = key_head(hv, Hk, Hv, flags);
 
     const ET *kp = k + ((size_t)b * Hk + hk) * DK;
     const ET *qp = q + ((size_t)b * Hk + hk) * DK;
@@ -67,7 +67,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         bq += __shfl_xor(bq, off);
         kq += __shfl_xor(kq, off);
     }
-    const float gt = g[slot], bt = beta[slot];
+    const float gt = decay_of(g[slot], flags), bt = beta[slot];
     const float vj = to_f32(v[(size_t)slot * Dv + j]);
     const float d = bt * (vj - gt * a);
 #pragma unroll
@@ -85,7 +85,7 @@ static hipError_t launch_step_inst(const FwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((step_kernel<ET, DK>), grid, block, 0, st,
                        static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                        static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                       static_cast<ET *>(a.y), a.Hk, a.Hv, a.Dv, a.scale);
+                       static_cast<ET *>(a.y), a.Hk, a.Hv, a.Dv, a.scale, a.flags);
     return hipGetLastError();
 }
 
@@ -154,7 +154,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 const ET *__restrict__ v, const float *__restrict__ g,
                 const float *__restrict__ beta, const float *state_in,
                 float *state_out, ET *__restrict__ y,
-                int T, int Hk, int Hv, int Dv, float scale)
+                int T, int Hk, int Hv, int Dv, float scale, int flags)
 {
     constexpr int NP = DK / 32;                   // 16-byte pieces per lane and row
     constexpr int ROWS = 32 * R;                  // value rows per workgroup
@@ -164,7 +164,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const int blocks_per_slot = Dv / ROWS;
     const int slot = blockIdx.x / blocks_per_slot;
     const int j0 = (blockIdx.x - slot * blocks_per_slot) * ROWS + (tid >> 3) * R;
-    const int hv = slot % Hv, b = slot / Hv, hk = hv / (Hv / Hk);
+    const int hv = slot % Hv, b = slot / Hv, hk = key_head(hv, Hk, Hv, flags);
     const size_t qks = (size_t)Hk * DK, vs = (size_t)Hv * Dv;
     const ET *kp = k + ((size_t)b * T * Hk + hk) * DK + 4 * sub;
     const ET *qp = q + ((size_t)b * T * Hk + hk) * DK + 4 * sub;
@@ -203,7 +203,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             qv[m] = to_f32x4<ET>(qn[m]);
         }
         const typename RV::T vt = vn;
-        const float gt = gn, bt = bn;
+        const float gt = decay_of(gn, flags), bt = bn;
         if (t + 1 < T) load(t + 1);
         c *= gt;
         if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the slot
@@ -258,7 +258,7 @@ static hipError_t launch_seq_inst(const FwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((seq_kernel<ET, DK, R>), grid, dim3(256), 0, st,
                        static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                        static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, a.scale);
+                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, a.scale, a.flags);
     return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ enum {
     GDN_OK = 0,
     GDN_ERR_NULL = -1,        /* a required pointer is NULL                  */
     GDN_ERR_SHAPE = -2,       /* negative size, or Hv not a multiple of Hk   */
-    GDN_ERR_UNSUPPORTED = -3, /* Dk, Dv or C outside the supported set       */
+    GDN_ERR_UNSUPPORTED = -3, /* Dk, Dv, C or flags outside the supported set */
     GDN_ERR_ALIAS = -4,       /* an output overlaps another buffer           */
     GDN_ERR_ALIGN = -5,       /* a pointer is not 16-byte (4 for g, beta) aligned */
     GDN_ERR_HIP = -6,         /* a HIP launch failed                         */
@@ -136,6 +136,45 @@ int gdn_step(const void *q, const void *k, const void *v,
              const float *state_in, float *state_out, void *y,
              int B, int Hk, int Hv, int Dk, int Dv,
              gdn_dtype dtype, hipStream_t stream);
+
+/*
+ * Conventions of the ferrox-core gdn_chunk.rs page's host body, which takes
+ * the same rule with a choice of head map and with the gate given as the
+ * logarithm of the decay (it exponentiates the gate before use).  The _ex
+ * entry points take them as bits of `flags`:
+ *
+ *   GDN_HEADS_TILED   key head of value head hv is hv mod Hk (the tiled map:
+ *                     the Hk key heads repeat across the value heads)
+ *                     instead of hv / (Hv/Hk) (the grouped map).
+ *   GDN_GATE_LOG      g holds log(decay); the decay used is exp(g), so g = 0
+ *                     keeps the state and g = -inf forgets it.
+ *
+ * flags = 0 is exactly gdn_chunk_fwd / gdn_seq_fwd / gdn_step.  Any other
+ * bit is GDN_ERR_UNSUPPORTED.  All other arguments, layouts, alignment,
+ * aliasing and errors as for the entry points without _ex.
+ */
+enum {
+    GDN_HEADS_TILED = 1,
+    GDN_GATE_LOG = 2
+};
+
+int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                     const float *g, const float *beta,
+                     const float *state_in, float *state_out, void *y,
+                     int B, int T, int Hk, int Hv, int Dk, int Dv, int C, int flags,
+                     gdn_dtype dtype, hipStream_t stream);
+
+int gdn_seq_fwd_ex(const void *q, const void *k, const void *v,
+                   const float *g, const float *beta,
+                   const float *state_in, float *state_out, void *y,
+                   int B, int T, int Hk, int Hv, int Dk, int Dv, int flags,
+                   gdn_dtype dtype, hipStream_t stream);
+
+int gdn_step_ex(const void *q, const void *k, const void *v,
+                const float *g, const float *beta,
+                const float *state_in, float *state_out, void *y,
+                int B, int Hk, int Hv, int Dk, int Dv, int flags,
+                gdn_dtype dtype, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(int status);

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gdn_chunk_fwd", "gdn_seq_fwd", "gdn_step", "gdn_status_string", "gdn_version"} <= set(names)
+    assert {"gdn_chunk_fwd", "gdn_seq_fwd", "gdn_step", "gdn_chunk_fwd_ex", "gdn_seq_fwd_ex",
+            "gdn_step_ex", "gdn_status_string", "gdn_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
 
@@ -128,3 +129,26 @@ def test_empty_batch_is_a_no_op(lib):
     assert step(lib, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
     assert seq(lib, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
     assert chunk(lib, B=0, C=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
+
+
+def chunk_ex(lib, flags, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=6 * A, so=7 * A, y=8 * A,
+             B=1, T=4, Hk=1, Hv=1, Dk=32, Dv=32, C=16, dtype=1):
+    return lib.gdn_chunk_fwd_ex(P(q), P(k), P(v), P(g), P(b), P(si), P(so), P(y),
+                                B, T, Hk, Hv, Dk, Dv, C, flags, dtype, None)
+
+
+def test_ex_flags(lib):
+    """Unknown flag bits are rejected; known ones pass the host checks (B = 0
+    stops before any launch); the _ex calls check arguments like the plain
+    ones."""
+    for bad in (4, 8, 1 << 30, -1):
+        assert chunk_ex(lib, bad) == UNSUP
+        assert lib.gdn_seq_fwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A),
+                                  P(8 * A), 1, 4, 1, 1, 32, 32, bad, 1, None) == UNSUP
+        assert lib.gdn_step_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A),
+                               P(8 * A), 1, 1, 1, 32, 32, bad, 1, None) == UNSUP
+    for good in (0, 1, 2, 3):
+        assert chunk_ex(lib, good, B=0, q=0, k=0, v=0, g=0, b=0, si=0, so=0, y=0) == OK
+        assert chunk_ex(lib, good, Hk=2, Hv=3) == SHAPE
+        assert chunk_ex(lib, good, C=8) == UNSUP
+        assert chunk_ex(lib, good, y=2 * A) == ALIAS
