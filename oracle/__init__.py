@@ -50,7 +50,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.gdn_ref_forward.argtypes = [dp] * 8 + [ctypes.c_long] * 6 + [
-            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         lib.gdn_ref_forward.restype = ctypes.c_int
         lib.gdn_ref_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -95,15 +95,18 @@ def forward(q, k, v, g, beta, state=None, *, slot_mask=None, nthreads=0,
     ``(y, state_out)`` in float64.  ``slot_mask`` (bool [B,Hv]) restricts
     the work to some slots; the others come back as NaN.  ``head_map``
     picks the key head of each value head (:func:`key_heads`); ``gate`` says
-    whether ``g`` is the decay or its natural logarithm.
+    whether ``g`` is the decay or its natural logarithm.  ``g`` may also be
+    [B,T,Hv,Dk]: one decay per key dimension, scaling the state's key
+    columns.
     """
     if head_map not in HEAD_MAPS or gate not in GATES:
         raise ValueError("head_map / gate")
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
-    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) \
-            or beta.shape != (B, T, Hv):
+    vector_gate = g.ndim == 4
+    if k.shape != q.shape or v.shape[:2] != (B, T) or beta.shape != (B, T, Hv) \
+            or g.shape != ((B, T, Hv, Dk) if vector_gate else (B, T, Hv)):
         raise ValueError("inconsistent shapes")
     s_in = None if state is None else _f64(state)
     if s_in is not None and s_in.shape != (B, Hv, Dv, Dk):
@@ -116,6 +119,7 @@ def forward(q, k, v, g, beta, state=None, *, slot_mask=None, nthreads=0,
     rc = _load().gdn_ref_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s_in), _ptr(s_out),
         _ptr(y), B, T, Hk, Hv, Dk, Dv, HEAD_MAPS.index(head_map), GATES.index(gate),
+        int(vector_gate),
         None if mask is None else mask.ctypes.data_as(ctypes.c_void_p), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"gdn_ref_forward failed ({rc})")
@@ -126,7 +130,8 @@ def forward_numpy(q, k, v, g, beta, state=None, *, head_map="grouped", gate="dec
     """Sequential rule in NumPy, float64 (tiny cases).
 
     Same contract as :func:`forward`.  Token loop; every slot advances at
-    once: the value head ``hv`` reads key head ``key_heads(...)[hv]``.
+    once: the value head ``hv`` reads key head ``key_heads(...)[hv]``; a
+    [B,T,Hv,Dk] gate decays each key column of the state by its own factor.
     """
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     B, T, Hk, Dk = q.shape
@@ -144,7 +149,7 @@ def forward_numpy(q, k, v, g, beta, state=None, *, head_map="grouped", gate="dec
     for t in range(T):
         kt = k[:, t][:, head_of]                  # [B,Hv,Dk]
         qt = q[:, t][:, head_of]
-        gt = g[:, t][..., None, None]             # [B,Hv,1,1]
+        gt = g[:, t][..., None, :] if g.ndim == 4 else g[:, t][..., None, None]   # [B,Hv,1,Dk|1]
         bt = beta[:, t][..., None]                # [B,Hv,1]
         S = gt * S                                # decay first
         d = bt * (v[:, t] - np.einsum("bhjd,bhd->bhj", S, kt))

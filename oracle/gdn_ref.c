@@ -25,6 +25,13 @@
  * Gate input: the decay itself (log_gate 0), or its natural logarithm
  * (log_gate 1), which the ferrox-core page's host body turns into the decay
  * with exp before use.
+ * Gate shape: one decay per (token, value head), g [B,T,Hv] (vector_gate 0),
+ * or one per key dimension, g [B,T,Hv,Dk] (vector_gate 1): the 4-D gate the
+ * MLX pull request page names ("Out of scope": a vector gate of shape
+ * [B, T, Hv, Dk]).  Read as a decay of each key column of the state:
+ *     S_t = S_{t-1} diag(g_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ * i.e. S[j][i] is multiplied by g_t[i] before the prediction, exactly where
+ * the scalar gate multiplies the whole state.
  *
  * Everything is float64 with plain loops in token order.  Slots (b, hv) are
  * independent (ferrox-core page: "Heads are independent") and run on an
@@ -46,12 +53,14 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
                     const double *g, const double *beta,
                     const double *state_in, double *state_out, double *y,
                     long B, long T, long Hk, long Hv, long Dk, long Dv,
-                    int head_map, int log_gate,
+                    int head_map, int log_gate, int vector_gate,
                     const unsigned char *slot_mask, int nthreads)
 {
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0) return -1;
     if (Hv % Hk != 0) return -1;
-    if ((head_map != 0 && head_map != 1) || (log_gate != 0 && log_gate != 1)) return -1;
+    if ((head_map != 0 && head_map != 1) || (log_gate != 0 && log_gate != 1) ||
+        (vector_gate != 0 && vector_gate != 1)) return -1;
+    const long gdim = vector_gate ? Dk : 1;      /* decays per (token, head) */
     if (!state_out) return -1;
     if (T > 0 && (!q || !k || !v || !g || !beta || !y)) return -1;
     const long group = Hv / Hk;
@@ -68,8 +77,9 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
         const long hk = head_map == 1 ? hv % Hk : hv / group;
         double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk));
         double *pred = (double *)malloc(sizeof(double) * (size_t)Dv);
-        if (!S || !pred) {
-            free(S); free(pred);
+        double *gv = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (!S || !pred || !gv) {
+            free(S); free(pred); free(gv);
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
@@ -82,21 +92,27 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
             const double *kt = k + ((b * T + t) * Hk + hk) * Dk;
             const double *qt = q + ((b * T + t) * Hk + hk) * Dk;
             const double *vt = v + ((b * T + t) * Hv + hv) * Dv;
-            const double gin = g[(b * T + t) * Hv + hv];
-            const double gt = log_gate ? exp(gin) : gin;
+            /* the decay of every key column i of the state */
+            const double *gin = g + ((b * T + t) * Hv + hv) * gdim;
+            for (long i = 0; i < Dk; ++i) {
+                const double x = gin[vector_gate ? i : 0];
+                gv[i] = log_gate ? exp(x) : x;
+            }
             const double bt = beta[(b * T + t) * Hv + hv];
             double *yt = y + ((b * T + t) * Hv + hv) * Dv;
-            /* prediction from the decayed previous state: g_t S_{t-1} k_t */
+            /* the decayed previous state, g_t S_{t-1} (column i by gv[i]) */
+            for (long j = 0; j < Dv; ++j)
+                for (long i = 0; i < Dk; ++i) S[j * Dk + i] *= gv[i];
+            /* prediction from the decayed state */
             for (long j = 0; j < Dv; ++j) {
                 double acc = 0.0;
                 for (long i = 0; i < Dk; ++i) acc += S[j * Dk + i] * kt[i];
-                pred[j] = gt * acc;
+                pred[j] = acc;
             }
             /* d_t and the rank-one update of the decayed state */
             for (long j = 0; j < Dv; ++j) {
                 const double dj = bt * (vt[j] - pred[j]);
-                for (long i = 0; i < Dk; ++i)
-                    S[j * Dk + i] = gt * S[j * Dk + i] + dj * kt[i];
+                for (long i = 0; i < Dk; ++i) S[j * Dk + i] += dj * kt[i];
             }
             /* read-out of the updated state */
             for (long j = 0; j < Dv; ++j) {
@@ -108,6 +124,7 @@ int gdn_ref_forward(const double *q, const double *k, const double *v,
         memcpy(state_out + slot * Dv * Dk, S, sizeof(double) * (size_t)(Dv * Dk));
         free(S);
         free(pred);
+        free(gv);
     }
     return failed ? -2 : 0;
 }

@@ -396,3 +396,79 @@ def _option_mutant(kind):
 def test_option_mistake_is_caught(kind, check):
     with np.errstate(all="ignore"):
         assert not check(_option_mutant(kind))
+
+
+# ----------------------------------------------------- per-key-dimension gate
+# A gate g [B,T,Hv,Dk] decays each key column of the state by its own factor
+# (the 4-D "vector" gate the MLX pull request page names).  Pins: a vector of
+# equal entries is the scalar gate; with beta = 0 nothing is written and the
+# state's columns decay by the running products of their gates (closed form);
+# with beta = 1 and a unit key the written value is read back exactly, for
+# any gate; relabelling the key dimensions relabels the state's columns.
+
+def check_vector_gate(fwd):
+    rng = np.random.default_rng(41)
+    ok = True
+    q, k, v, g, beta, S0 = rand_case(rng, B=2, T=6, Hk=1, Hv=2, Dk=5, Dv=3)
+    gv = np.repeat(g[..., None], 5, axis=-1)
+    y1, s1 = fwd(q, k, v, gv, beta, S0)
+    y2, s2 = fwd(q, k, v, g, beta, S0)
+    ok &= np.allclose(y1, y2, rtol=1e-13, atol=1e-14) and np.allclose(s1, s2, rtol=1e-13, atol=1e-14)
+    # beta = 0: S_t = S0 diag(prod_{s<=t} g_s), y_t = S_t q_t / sqrt(Dk)
+    gv = rng.uniform(0.0, 1.0, (2, 6, 2, 5))
+    gv[0, 2, 1, 3] = 0.0
+    y, s = fwd(q, k, v, gv, np.zeros_like(beta), S0)
+    cum = np.cumprod(gv, axis=1)                                # [B,T,Hv,Dk]
+    want_s = S0 * cum[:, -1][:, :, None, :]
+    want_y = np.einsum("bhji,bthi,bti->bthj", S0, cum, q[:, :, 0]) / np.sqrt(5)
+    ok &= np.allclose(s, want_s, rtol=0, atol=1e-14) and np.allclose(y, want_y, rtol=0, atol=1e-14)
+    # beta = 1, unit key: S_t k_t = v_t whatever the gate
+    _, k1, v1, _, _, S1 = rand_case(rng, B=1, T=1, Hk=1, Hv=1, Dk=5, Dv=3)
+    g1 = rng.uniform(0.1, 1.0, (1, 1, 1, 5))
+    _, st = fwd(q[:1, :1, :1], k1, v1, g1, np.ones((1, 1, 1)), S1)
+    ok &= np.allclose(st[0, 0] @ k1[0, 0, 0], v1[0, 0, 0], rtol=0, atol=1e-14)
+    # relabelling key dimensions
+    p = rng.permutation(5)
+    y, s = fwd(q, k, v, gv, beta, S0)
+    yp, sp = fwd(q[..., p], k[..., p], v, gv[..., p], beta, S0[..., p])
+    ok &= np.allclose(yp, y, rtol=0, atol=1e-13) and np.allclose(sp, s[..., p], rtol=0, atol=1e-13)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("name", list(ORACLES))
+def test_oracle_vector_gate(name):
+    assert check_vector_gate(ORACLES[name])
+
+
+def _vector_gate_mutant(kind):
+    def fwd(q, k, v, g, beta, state=None):
+        if g.ndim == 3:
+            return oracle.forward_numpy(q, k, v, g, beta, state)
+        B, T, Hk, Dk = q.shape
+        Hv, Dv = v.shape[2], v.shape[3]
+        S = np.zeros((B, Hv, Dv, Dk)) if state is None else np.array(state, dtype=np.float64)
+        y = np.empty((B, T, Hv, Dv))
+        for t in range(T):
+            kt, qt = k[:, t][:, [0] * Hv], q[:, t][:, [0] * Hv]
+            gt = g[:, t]
+            if kind == "gate_on_value_rows":
+                Sd = S * gt[..., :Dv, None] if Dv <= Dk else S
+            elif kind == "gate_mean":
+                Sd = S * gt.mean(-1)[..., None, None]
+            else:
+                Sd = S * gt[..., None, :]
+            pred = np.einsum("bhji,bhi->bhj", S if kind == "undecayed_prediction" else Sd, kt)
+            d = beta[:, t][..., None] * (v[:, t] - pred)
+            S = Sd + d[..., :, None] * kt[..., None, :]
+            y[:, t] = np.einsum("bhji,bhi->bhj", S, qt) / np.sqrt(Dk)
+        return y, S
+    return fwd
+
+
+@pytest.mark.parametrize("kind", ["gate_on_value_rows", "gate_mean", "undecayed_prediction"])
+def test_vector_gate_mistake_is_caught(kind):
+    assert not check_vector_gate(_vector_gate_mutant(kind))
+
+
+def test_vector_gate_harness_passes_unmutated():
+    assert check_vector_gate(_vector_gate_mutant("none"))
