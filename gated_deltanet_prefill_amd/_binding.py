@@ -18,7 +18,7 @@ GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
 SUPPORTED_DIMS = (32, 64, 128)
 SUPPORTED_CHUNKS = (0, 16, 32, 64)     # 0: the library chooses
-GDN_HEADS_TILED, GDN_GATE_LOG = 1, 2
+GDN_HEADS_TILED, GDN_GATE_LOG, GDN_GATE_VECTOR = 1, 2, 4
 HEAD_MAPS = ("grouped", "tiled")
 GATES = ("decay", "log")
 
@@ -86,12 +86,13 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _flags(heads, gate):
+def _flags(heads, gate, vector=False):
     if heads not in HEAD_MAPS:
         raise ValueError(f"heads must be one of {HEAD_MAPS}")
     if gate not in GATES:
         raise ValueError(f"gate must be one of {GATES}")
-    return (GDN_HEADS_TILED if heads == "tiled" else 0) | (GDN_GATE_LOG if gate == "log" else 0)
+    return ((GDN_HEADS_TILED if heads == "tiled" else 0) | (GDN_GATE_LOG if gate == "log" else 0)
+            | (GDN_GATE_VECTOR if vector else 0))
 
 
 def _prefill_args(q, k, v, g, beta, state_in, state_out, y):
@@ -103,7 +104,7 @@ def _prefill_args(q, k, v, g, beta, state_in, state_out, y):
     _check_tensor("q", q, (B, T, Hk, Dk), dt, dev)
     _check_tensor("k", k, (B, T, Hk, Dk), dt, dev)
     _check_tensor("v", v, (B, T, Hv, Dv), dt, dev)
-    _check_tensor("g", g, (B, T, Hv), torch.float32, dev)
+    _check_tensor("g", g, (B, T, Hv, Dk) if g.dim() == 4 else (B, T, Hv), torch.float32, dev)
     _check_tensor("beta", beta, (B, T, Hv), torch.float32, dev)
     if state_in is not None:
         _check_tensor("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
@@ -121,7 +122,7 @@ def seq_fwd(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=N
     """``gdn_seq_fwd_ex`` on torch tensors (token by token, the state read
     once).  Arguments and result as for :func:`chunk_fwd` (without ``C``)."""
     lib = load()
-    flags = _flags(heads, gate)
+    flags = _flags(heads, gate, g.dim() == 4)
     (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
     rc = lib.gdn_seq_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                             _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, flags,
@@ -141,10 +142,11 @@ def chunk_fwd(q, k, v, g, beta, state_in=None, *, C=64, state_out=None, y=None,
     ``C = 0`` lets the library choose the kernel and the chunk length.
     ``heads`` is the head map ("grouped": key head hv // (Hv // Hk);
     "tiled": hv % Hk) and ``gate`` says whether ``g`` is the decay or its
-    natural logarithm ("decay" / "log").
+    natural logarithm ("decay" / "log").  ``g`` [B,T,Hv,Dk] is a decay per
+    key dimension (each key column of the state decays by its own factor).
     """
     lib = load()
-    flags = _flags(heads, gate)
+    flags = _flags(heads, gate, g.dim() == 4)
     (B, T, Hk, Hv, Dk, Dv, dev, dt), state_out, y = _prefill_args(q, k, v, g, beta, state_in, state_out, y)
     rc = lib.gdn_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                               _ptr(state_out), _ptr(y), B, T, Hk, Hv, Dk, Dv, int(C), flags,
@@ -160,10 +162,11 @@ def step(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None
 
     q, k [B,Hk,Dk]; v [B,Hv,Dv]; g, beta [B,Hv] float32; state_in
     [B,Hv,Dv,Dk] float32 or None; ``state_out`` may be ``state_in``.
-    ``heads`` and ``gate`` as for :func:`chunk_fwd`.
+    ``heads`` and ``gate`` as for :func:`chunk_fwd`; ``g`` [B,Hv,Dk] is a
+    decay per key dimension.
     """
     lib = load()
-    flags = _flags(heads, gate)
+    flags = _flags(heads, gate, g.dim() == 3)
     B, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     dev, dt = q.device, q.dtype
@@ -172,7 +175,7 @@ def step(q, k, v, g, beta, state_in=None, *, state_out=None, y=None, stream=None
     _check_tensor("q", q, (B, Hk, Dk), dt, dev)
     _check_tensor("k", k, (B, Hk, Dk), dt, dev)
     _check_tensor("v", v, (B, Hv, Dv), dt, dev)
-    _check_tensor("g", g, (B, Hv), torch.float32, dev)
+    _check_tensor("g", g, (B, Hv, Dk) if g.dim() == 3 else (B, Hv), torch.float32, dev)
     _check_tensor("beta", beta, (B, Hv), torch.float32, dev)
     if state_in is not None:
         _check_tensor("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)

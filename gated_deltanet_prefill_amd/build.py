@@ -26,7 +26,8 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 SOURCES = ["gdn_api.cpp", "gdn_step.hip", "gdn_chunk_f32.hip",
-           "gdn_chunk_bf16.hip", "gdn_chunk_f16.hip"]
+           "gdn_chunk_bf16.hip", "gdn_chunk_f16.hip", "gdn_chunk_vg_f32.hip",
+           "gdn_chunk_vg_bf16.hip", "gdn_chunk_vg_f16.hip"]
 
 
 def _compile(src: str) -> str:

@@ -12,9 +12,9 @@
 
 namespace {
 
-static_assert(GDN_HEADS_TILED == gdn::kTiledHeads && GDN_GATE_LOG == gdn::kLogGate,
-              "flag values of the ABI and the kernels");
-constexpr int kKnownFlags = GDN_HEADS_TILED | GDN_GATE_LOG;
+static_assert(GDN_HEADS_TILED == gdn::kTiledHeads && GDN_GATE_LOG == gdn::kLogGate &&
+              GDN_GATE_VECTOR == gdn::kVectorGate, "flag values of the ABI and the kernels");
+constexpr int kKnownFlags = GDN_HEADS_TILED | GDN_GATE_LOG | GDN_GATE_VECTOR;
 
 struct Range {
     uintptr_t lo, hi;                 // [lo, hi); empty when lo == hi
@@ -35,12 +35,13 @@ bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
 
 int elem_size(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
 
-// Shared checks of both entry points; T = 1 for the step.
+// Shared checks of the entry points; T = 1 for the step.
 int check(const void *q, const void *k, const void *v, const float *g,
           const float *beta, const float *state_in, const float *state_out,
           const void *y, long B, long T, long Hk, long Hv, long Dk, long Dv,
-          int dtype)
+          int dtype, int flags = 0)
 {
+    const bool vg = (flags & GDN_GATE_VECTOR) != 0;
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0) return GDN_ERR_SHAPE;
     if (Hv % Hk != 0) return GDN_ERR_SHAPE;
     if (B * Hv * (Dv / 32 > 0 ? Dv / 32 : 1) > INT32_MAX) return GDN_ERR_SHAPE;
@@ -52,14 +53,15 @@ int check(const void *q, const void *k, const void *v, const float *g,
     const void *p16[] = {q, k, v, y, state_in, state_out};
     for (const void *p : p16)
         if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
-    if ((g && !aligned(g, 4)) || (beta && !aligned(beta, 4))) return GDN_ERR_ALIGN;
+    if ((g && !aligned(g, vg ? 16 : 4)) || (beta && !aligned(beta, 4))) return GDN_ERR_ALIGN;
 
     const uint64_t es = (uint64_t)elem_size(dtype);
     const uint64_t nqk = (uint64_t)B * T * Hk * Dk, nv = (uint64_t)B * T * Hv * Dv;
     const uint64_t ngb = (uint64_t)B * T * Hv, ns = (uint64_t)B * Hv * Dv * Dk;
     const Range rq = range_of(T ? q : nullptr, nqk * es), rk = range_of(T ? k : nullptr, nqk * es);
     const Range rv = range_of(T ? v : nullptr, nv * es), ry = range_of(T ? y : nullptr, nv * es);
-    const Range rg = range_of(T ? g : nullptr, ngb * 4), rb = range_of(T ? beta : nullptr, ngb * 4);
+    const Range rg = range_of(T ? g : nullptr, ngb * (vg ? (uint64_t)Dk : 1) * 4);
+    const Range rb = range_of(T ? beta : nullptr, ngb * 4);
     const Range rsi = range_of(state_in, ns * 4), rso = range_of(state_out, ns * 4);
     // y overlaps nothing; state_out overlaps nothing but (exactly) state_in
     const Range others_y[] = {rq, rk, rv, rg, rb, rsi, rso};
@@ -99,6 +101,10 @@ int chunk_for(int dtype, int Dk, int Dv, long slots, int T) {
 int launch(const gdn::FwdArgs &a, int dtype, bool seq, hipStream_t stream) {
     hipError_t e;
     if (seq) e = gdn::launch_seq(dtype, a, stream);
+    else if (a.flags & gdn::kVectorGate)
+        e = dtype == GDN_F32 ? gdn::launch_chunk_vg_f32(a, stream)
+          : dtype == GDN_BF16 ? gdn::launch_chunk_vg_bf16(a, stream)
+          : gdn::launch_chunk_vg_f16(a, stream);
     else if (dtype == GDN_F32) e = gdn::launch_chunk_f32(a, stream);
     else if (dtype == GDN_BF16) e = gdn::launch_chunk_bf16(a, stream);
     else e = gdn::launch_chunk_f16(a, stream);
@@ -115,7 +121,7 @@ int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v,
                      int B, int T, int Hk, int Hv, int Dk, int Dv, int C, int flags,
                      gdn_dtype dtype, hipStream_t stream)
 {
-    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype, flags);
     if (rc != GDN_OK) return rc;
     if (C != 0 && C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
@@ -143,7 +149,7 @@ int gdn_seq_fwd_ex(const void *q, const void *k, const void *v,
                    int B, int T, int Hk, int Hv, int Dk, int Dv, int flags,
                    gdn_dtype dtype, hipStream_t stream)
 {
-    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype);
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, (int)dtype, flags);
     if (rc != GDN_OK) return rc;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
@@ -168,7 +174,7 @@ int gdn_step_ex(const void *q, const void *k, const void *v,
                 int B, int Hk, int Hv, int Dk, int Dv, int flags,
                 gdn_dtype dtype, hipStream_t stream)
 {
-    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, 1, Hk, Hv, Dk, Dv, (int)dtype);
+    int rc = check(q, k, v, g, beta, state_in, state_out, y, B, 1, Hk, Hv, Dk, Dv, (int)dtype, flags);
     if (rc != GDN_OK) return rc;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
@@ -194,15 +200,15 @@ const char *gdn_status_string(int status)
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "a required pointer is NULL";
     case GDN_ERR_SHAPE: return "invalid shape (negative size, or Hv not a multiple of Hk)";
-    case GDN_ERR_UNSUPPORTED: return "unsupported size or flag (Dk, Dv must be 32, 64 or 128; C must be 0, 16, 32 or 64; flags only GDN_HEADS_TILED | GDN_GATE_LOG)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size or flag (Dk, Dv must be 32, 64 or 128; C must be 0, 16, 32 or 64; flags only GDN_HEADS_TILED | GDN_GATE_LOG | GDN_GATE_VECTOR)";
     case GDN_ERR_ALIAS: return "an output overlaps another buffer";
-    case GDN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, y, state; 4 for g, beta)";
+    case GDN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, y, state and a per-key-dimension g; 4 for a scalar g and beta)";
     case GDN_ERR_HIP: return "HIP launch failed";
     case GDN_ERR_DTYPE: return "unknown dtype";
     default: return "unknown status";
     }
 }
 
-int gdn_version(void) { return 10200; }
+int gdn_version(void) { return 10300; }
 
 }  // extern "C"

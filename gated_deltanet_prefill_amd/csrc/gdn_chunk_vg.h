@@ -1,0 +1,596 @@
+// gdn_chunk_vg.h -- the chunked forward kernel for a decay per key dimension.
+//
+// The gate g [B,T,Hv,Dk] decays each key column of the state on its own:
+//     S_t = S_{t-1} diag(g_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+// (the 4-D gate the MLX pull request page "Pack gated_delta_seq" names as a
+// shape its kernels would misread).  Within a chunk the decay ratio between
+// tokens j <= t becomes a vector over key dimensions,
+//     R_i[t][j] = g_{j+1,i} ... g_{t,i},
+// so it no longer factors out of K K^T: every product that carries a ratio
+// is formed from operands scaled per key dimension, with each scale a
+// product of decays (never a quotient; the ferrox-core gdn_chunk.rs page,
+// "The algebra") and therefore at most 1 for decays in [0, 1]:
+//
+//  * tokens in different 16-token blocks (j in block 0, t in block 1):
+//        R[t][j] = P_t S_j,  P_t = prefix product of t's block up to t,
+//                            S_j = product over j's block after j;
+//  * tokens in one 16-token block: with m the highest bit in which their
+//    in-block indices differ, t lies in the upper and j in the lower half of
+//    an aligned segment of 2^(m+1) tokens, and
+//        R[t][j] = L^m_t E^m_j,  L^m_t = product over t's half up to t,
+//                                E^m_j = product over j's half after j;
+//    the block's K K^T and Q K^T are then four products, one per level m,
+//    each kept where its level applies.  The segment products come from
+//    cross-lane scans (DPP) over the block's sixteen tokens, one per lane.
+//
+// With G_t = prod_{s<=t} g_s and G_last = G_{c-1} (per key dimension):
+//     A[t][j] = beta_t sum_i k_ti k_ji R_i[t][j]  (j < t),
+//     QKR[t][j] = sum_i q_ti k_ji R_i[t][j] / sqrt(Dk)  (j <= t),
+//     D = (I + A)^-1 beta (V - (K diag G) S0^T),
+//     y = ((Q diag G) S0^T) / sqrt(Dk) + QKR D,
+//     S <- S0 diag(G_last) + D^T (K diag(G_last / G)),
+// where G_last / G_t = prod_{s>t} g_s is again a product of decays.
+//
+// The layout and the substitution follow the generic chunk kernel
+// (gdn_chunk_impl.h); chunks are at most 32 tokens (two 16-token blocks)
+// so that the gate tiles fit in LDS, 16 for float32 inputs.
+
+#pragma once
+
+#include "gdn_chunk_impl.h"
+
+namespace gdn {
+
+template <typename ET, int DK_, int DVS_, int C_, int NB_>
+struct VgCfg : ChunkCfg<ET, DK_, DVS_, C_, NB_> {
+    using Base = ChunkCfg<ET, DK_, DVS_, C_, NB_>;
+    static constexpr int LDG = DK_ + 4;                   // f32 rows of decays / scans
+    static constexpr int oGv = Base::BYTES;               // decays [C][LDG]
+    static constexpr int oP16 = oGv + C_ * LDG * 4;       // in-block prefix products
+    static constexpr int oS16 = oP16 + C_ * LDG * 4;      // in-block products after t
+    static constexpr int oBT = oS16 + C_ * LDG * 4;       // block totals [NBT][DK]
+    static constexpr int oGl = oBT + Base::NBT * DK_ * 4; // chunk totals [DK]
+    static constexpr int oKg = oGl + DK_ * 4;             // K diag(G)       [C][LDK]
+    static constexpr int oQg = oKg + C_ * Base::LDK * Base::ES;   // Q diag(G)
+    static constexpr int oKr = oQg + C_ * Base::LDK * Base::ES;   // K diag(G_last / G)
+    static constexpr int VBYTES = oKr + C_ * Base::LDK * Base::ES;
+    static constexpr int GUNITS = C_ * DK_ / 4;           // 16-byte units of a chunk's gates
+    static constexpr int PERG = (GUNITS + Base::NT - 1) / Base::NT;
+    static_assert(VBYTES <= 160 * 1024, "LDS budget");
+    static_assert(Base::NBT <= 2 && Base::NBT <= Base::NW, "one wave per 16-token block");
+};
+
+// Products over aligned segments of the sixteen tokens of a block, one token
+// per lane of a DPP row (x = lane index in the row).  Segment sizes 2, 4, 8
+// and 16; "prefix" includes the lane's own token, "after" excludes it.
+struct SegScan {
+    float p[5];       // p[m]: product over the lane's 2^m segment up to and including it
+    float e[5];       // e[m]: product over the lane's 2^m segment after it
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_keep(float v) {   // DPP move, 1 where no source
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Every cross-lane move below is issued by all sixteen lanes before any
+// lane-dependent choice: a DPP move inside a branch would read lanes the
+// branch has switched off.
+__device__ __forceinline__ SegScan seg_scan(float g, int x) {
+    SegScan r;
+    // inclusive prefix: upper halves multiply by the total of their lower half
+    const float p0 = g;
+    const float a1 = dpp_row_shr<1>(p0);
+    const float p1 = (x & 1) ? p0 * a1 : p0;
+    const float a2 = quad_bcast<1>(p1);
+    const float p2 = (x & 2) ? p1 * a2 : p1;
+    const float a3 = dpp_row_shr<4>(quad_bcast<3>(p2));           // lower quad's total, one quad up
+    const float p3 = (x & 4) ? p2 * a3 : p2;
+    const float w3 = quad_bcast<3>(p3);
+    const float w3a = dpp_row_shr<4>(w3);
+    const float w3b = dpp_row_shr<4>(w3a);                        // lanes 8-11 / 12-15 get lane 7's
+    const float p4 = (x & 8) ? p3 * ((x & 4) ? w3b : w3a) : p3;
+    // inclusive suffix: lower halves multiply by the total of their upper half
+    const float s0 = g;
+    const float b1 = dpp_row_shl<1>(s0);
+    const float s1 = (x & 1) ? s0 : s0 * b1;
+    const float b2 = quad_bcast<2>(s1);
+    const float s2 = (x & 2) ? s1 : s1 * b2;
+    const float b3 = dpp_row_shl<4>(quad_bcast<0>(s2));           // upper quad's total, one quad down
+    const float s3 = (x & 4) ? s2 : s2 * b3;
+    const float v3 = quad_bcast<0>(s3);
+    const float v3a = dpp_row_shl<4>(v3);
+    const float v3b = dpp_row_shl<4>(v3a);                        // lanes 4-7 / 0-3 get lane 8's
+    const float s4 = (x & 8) ? s3 : s3 * ((x & 4) ? v3a : v3b);
+    r.p[0] = p0; r.p[1] = p1; r.p[2] = p2; r.p[3] = p3; r.p[4] = p4;
+    // exclusive suffix: the next lane's inclusive suffix when it is in the
+    // same segment, else the empty product
+    const float n1 = dpp_keep<0x101>(s1), n2 = dpp_keep<0x101>(s2),
+                n3 = dpp_keep<0x101>(s3), n4 = dpp_keep<0x101>(s4);
+    r.e[0] = 1.f;
+    r.e[1] = ((x + 1) & 1) ? n1 : 1.f;
+    r.e[2] = ((x + 1) & 3) ? n2 : 1.f;
+    r.e[3] = ((x + 1) & 7) ? n3 : 1.f;
+    r.e[4] = ((x + 1) & 15) ? n4 : 1.f;
+    return r;
+}
+
+// 16-bit: two 4-element pieces make one 8-element operand; f32: one piece.
+template <typename ET>
+__device__ __forceinline__ typename Step<ET>::frag frag_of(const f32x4 *pc) {
+    if constexpr (sizeof(ET) == 4) {
+        return pc[0];
+    } else {
+        return cat8<ET>(cvt4<ET>(pc[0]), cvt4<ET>(pc[1]));
+    }
+}
+
+template <typename ET, int DK, int DVS, int C, int NB>
+__global__ __launch_bounds__(4 * DVS / NB, 1)
+void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
+                     const ET *__restrict__ v, const float *__restrict__ g,
+                     const float *__restrict__ beta, const float *state_in,
+                     float *state_out, ET *__restrict__ y,
+                     int T, int Hk, int Hv, int Dv, int xcd_group, float scale, int flags)
+{
+    using L = VgCfg<ET, DK, DVS, C, NB>;
+    using X4 = typename Vec<ET>::x4;
+    using FR = typename Step<ET>::frag;
+    constexpr int BLK = Step<ET>::BLK;
+    constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDD = L::LDD,
+                  LDT = L::LDT, LDG = L::LDG, EPU = L::EPU;
+    constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
+    constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
+    static_assert(NBK % BLK == 0, "whole key steps");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::VBYTES];
+    ET *sK = reinterpret_cast<ET *>(smem + L::oK);
+    ET *sQ = reinterpret_cast<ET *>(smem + L::oQ);
+    ET *sV = reinterpret_cast<ET *>(smem + L::oV);
+    ET *sAn = reinterpret_cast<ET *>(smem + L::oAn);    // -A (16-bit)
+    ET *sQKR = reinterpret_cast<ET *>(smem + L::oQKR);
+    float *sAd = reinterpret_cast<float *>(smem + L::oAd);  // diagonal blocks of A (f32)
+    ET *sTd = reinterpret_cast<ET *>(smem + L::oTd);    // diagonal blocks of (I + A)^-1
+    float *sb = reinterpret_cast<float *>(smem + L::oVec);
+    float *sGv = reinterpret_cast<float *>(smem + L::oGv);
+    float *sP16 = reinterpret_cast<float *>(smem + L::oP16);
+    float *sS16 = reinterpret_cast<float *>(smem + L::oS16);
+    float *sBT = reinterpret_cast<float *>(smem + L::oBT);
+    float *sGl = reinterpret_cast<float *>(smem + L::oGl);
+    ET *sKg = reinterpret_cast<ET *>(smem + L::oKg);
+    ET *sQg = reinterpret_cast<ET *>(smem + L::oQg);
+    ET *sKr = reinterpret_cast<ET *>(smem + L::oKr);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, x = lane & 15, qd = lane >> 4;
+    // XCD-grouped slot order, as in the generic kernel
+    int bid = blockIdx.x;
+    if (xcd_group > 1) {
+        const int xcd = bid & 7, kk = bid >> 3;
+        const int sib = kk % xcd_group, m = kk / xcd_group;
+        bid = (m * 8 + xcd) * xcd_group + sib;
+    }
+    const int b = bid / Hv, hv = value_head_of_rank(bid % Hv, Hk, Hv, flags);
+    const int hk = key_head(hv, Hk, Hv, flags);
+    const int slot = b * Hv + hv;
+    const int vloc = wave * 16 * NB;
+
+    f32x4 S[NBK][NB];
+    const size_t sbase = (size_t)slot * Dv * DK;
+#pragma unroll
+    for (int vb = 0; vb < NB; ++vb) {
+        const size_t row = sbase + (size_t)(vloc + 16 * vb + x) * DK;
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+            S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + 16 * kb + 4 * qd)
+                                 : zero4();
+    }
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+
+    // -A and QKR above the diagonal blocks stay zero
+    for (int i = tid; i < (L::oAd - L::oAn) / 16; i += NT)
+        reinterpret_cast<uint4 *>(smem + L::oAn)[i] = zero_u4();
+
+    const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * Dv, gstride = (size_t)Hv * DK;
+    const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
+    const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
+    const ET *vbase = v + ((size_t)b * T * Hv + hv) * Dv;
+    const float *gbase = g + ((size_t)b * T * Hv + hv) * DK;
+    const float *bbase = beta + (size_t)b * T * Hv + hv;
+
+    uint4 rk[L::PERK], rq[L::PERK], rv[L::PERV], rg[L::PERG];
+    float rb = 0.f;
+    auto prefetch = [&](int t0) {
+        const int last = min(C, T - t0) - 1;
+#pragma unroll
+        for (int i = 0; i < L::PERK; ++i) {
+            const int it = min(tid + i * NT, L::KIT - 1);
+            const int t = min(it / L::UPK, last), u = it % L::UPK;
+            rk[i] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(t0 + t) * kstride + u * EPU);
+            rq[i] = *reinterpret_cast<const uint4 *>(qbase + (size_t)(t0 + t) * kstride + u * EPU);
+        }
+#pragma unroll
+        for (int i = 0; i < L::PERV; ++i) {
+            const int it = min(tid + i * NT, L::VIT - 1);
+            const int t = min(it / L::UPV, last), u = it % L::UPV;
+            rv[i] = *reinterpret_cast<const uint4 *>(vbase + (size_t)(t0 + t) * vstride + u * EPU);
+        }
+#pragma unroll
+        for (int i = 0; i < L::PERG; ++i) {
+            const int it = min(tid + i * NT, L::GUNITS - 1);
+            const int t = min(it / (DK / 4), last), u = it % (DK / 4);
+            rg[i] = *reinterpret_cast<const uint4 *>(gbase + (size_t)(t0 + t) * gstride + 4 * u);
+        }
+        rb = bbase[(size_t)(t0 + min(tid, last)) * Hv];
+    };
+
+    // registers -> LDS; rows t >= cn: k = q = v = 0, g = 1, beta = 0
+    auto stage = [&](int cn) {
+#pragma unroll
+        for (int i = 0; i < L::PERK; ++i) {
+            asm volatile("" : "+v"(rk[i].x), "+v"(rk[i].y), "+v"(rk[i].z), "+v"(rk[i].w));
+            asm volatile("" : "+v"(rq[i].x), "+v"(rq[i].y), "+v"(rq[i].z), "+v"(rq[i].w));
+        }
+#pragma unroll
+        for (int i = 0; i < L::PERV; ++i)
+            asm volatile("" : "+v"(rv[i].x), "+v"(rv[i].y), "+v"(rv[i].z), "+v"(rv[i].w));
+#pragma unroll
+        for (int i = 0; i < L::PERG; ++i)
+            asm volatile("" : "+v"(rg[i].x), "+v"(rg[i].y), "+v"(rg[i].z), "+v"(rg[i].w));
+        asm volatile("" : "+v"(rb));
+#pragma unroll
+        for (int i = 0; i < L::PERK; ++i) {
+            const int it = tid + i * NT;
+            if (L::KIT % NT == 0 || it < L::KIT) {
+                const int t = it / L::UPK, u = it - t * L::UPK;
+                const bool pad = t >= cn;
+                *reinterpret_cast<uint4 *>(sK + t * LDK + u * EPU) = pad ? zero_u4() : rk[i];
+                *reinterpret_cast<uint4 *>(sQ + t * LDK + u * EPU) = pad ? zero_u4() : rq[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < L::PERV; ++i) {
+            const int it = tid + i * NT;
+            if (L::VIT % NT == 0 || it < L::VIT) {
+                const int t = it / L::UPV, u = it - t * L::UPV;
+                *reinterpret_cast<uint4 *>(sV + t * LDV + u * EPU) = (t >= cn) ? zero_u4() : rv[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < L::PERG; ++i) {
+            const int it = tid + i * NT;
+            if (L::GUNITS % NT == 0 || it < L::GUNITS) {
+                const int t = it / (DK / 4), u = it - t * (DK / 4);
+                f32x4 gv = __builtin_bit_cast(f32x4, rg[i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[e] = (t < cn) ? decay_of(gv[e], flags) : 1.f;
+                *reinterpret_cast<f32x4 *>(sGv + t * LDG + 4 * u) = gv;
+            }
+        }
+        if (tid < C) sb[tid] = (tid < cn) ? rb : 0.f;
+    };
+
+    const int nchunks = (T + C - 1) / C;
+    if (nchunks > 0) {
+        prefetch(0);
+        stage(min(C, T));
+    }
+
+    for (int n = 0; n < nchunks; ++n) {
+        const int t0 = n * C;
+        const int cn = min(C, T - t0);
+        if (n + 1 < nchunks) prefetch(t0 + C);
+        lds_barrier();                     // chunk n staged
+
+        // ---- (a) wave w < NBT: the scans of block w (P16, S16, block
+        // totals) and its diagonal tiles of K K^T and Q K^T, one product per
+        // level; lane x of each DPP row is token 16 w + x.
+        if (wave < NBT) {
+            const int bt = wave, t = 16 * bt + x;
+            f32x4 kk[4], qk[4], q0 = zero4();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) { kk[m] = zero4(); qk[m] = zero4(); }
+#pragma unroll
+            for (int s = 0; s < NSK; ++s) {
+                f32x4 ka[4][BLK], kl[4][BLK], ql[4][BLK], k0[BLK], qq[BLK];
+#pragma unroll
+                for (int h = 0; h < BLK; ++h) {
+                    const int kb = s * BLK + h, i0 = 16 * kb + 4 * qd;
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGv + t * LDG + i0);
+                    const f32x4 kf = to_f32x4<ET>(frag_row<ET>(sK, LDK, 16 * bt, 0, kb, x, qd));
+                    const f32x4 qf = to_f32x4<ET>(frag_row<ET>(sQ, LDK, 16 * bt, 0, kb, x, qd));
+                    f32x4 p16, s16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const SegScan sc = seg_scan(g4[e], x);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            ka[m][h][e] = kf[e] * sc.e[m];
+                            kl[m][h][e] = kf[e] * sc.p[m];
+                            ql[m][h][e] = qf[e] * sc.p[m];
+                        }
+                        p16[e] = sc.p[4];
+                        s16[e] = sc.e[4];
+                    }
+                    k0[h] = kf;
+                    qq[h] = qf;
+                    *reinterpret_cast<f32x4 *>(sP16 + t * LDG + i0) = p16;
+                    *reinterpret_cast<f32x4 *>(sS16 + t * LDG + i0) = s16;
+                    if (x == 15) *reinterpret_cast<f32x4 *>(sBT + bt * DK + i0) = p16;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const FR fa = frag_of<ET>(ka[m]);
+                    kk[m] = mfma_step(fa, frag_of<ET>(kl[m]), kk[m]);
+                    qk[m] = mfma_step(fa, frag_of<ET>(ql[m]), qk[m]);
+                }
+                q0 = mfma_step(frag_of<ET>(k0), frag_of<ET>(qq), q0);
+            }
+            // lane (x, qd) holds column t = 16 bt + x, rows j = 16 bt + 4 qd + r
+            const float bv = sb[t];
+            f32x4 a, o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jl = 4 * qd + r, d = jl ^ x;
+                const int m = d >= 8 ? 3 : d >= 4 ? 2 : d >= 2 ? 1 : 0;
+                const float zk = m == 3 ? kk[3][r] : m == 2 ? kk[2][r] : m == 1 ? kk[1][r] : kk[0][r];
+                const float zq = m == 3 ? qk[3][r] : m == 2 ? qk[2][r] : m == 1 ? qk[1][r] : qk[0][r];
+                a[r] = (jl < x) ? bv * zk : 0.f;
+                o[r] = (jl < x) ? scale * zq : (jl == x) ? scale * q0[r] : 0.f;
+            }
+            const int j0 = 16 * bt + 4 * qd;
+            st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
+            st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
+            *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
+        }
+        lds_barrier();
+
+        // ---- (b) diagonal inverses (waves < NBT); the tile between the two
+        // blocks (one more wave); the scaled K and Q for the state products
+        // and the update (every thread).
+        if (wave < NBT) {
+            const int base = 16 * wave;
+            const int p = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
+            f32x4 arow[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4)
+                    arow[m][j4] = *reinterpret_cast<const f32x4 *>(sAd + (base + p + 4 * m) * LDD + 4 * j4);
+            float s[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) s[m] = (p + 4 * m == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) {
+                float xj;
+                switch (j & 3) {
+                case 0: xj = quad_bcast<0>(s[j >> 2]); break;
+                case 1: xj = quad_bcast<1>(s[j >> 2]); break;
+                case 2: xj = quad_bcast<2>(s[j >> 2]); break;
+                default: xj = quad_bcast<3>(s[j >> 2]); break;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
+        }
+        if constexpr (NBT == 2) {
+            // tokens j in block 0, t in block 1: R = P16_t S16_j
+            if (wave == (NW > NBT ? NBT : 0)) {
+                f32x4 zk = zero4(), zq = zero4();
+#pragma unroll
+                for (int s = 0; s < NSK; ++s) {
+                    f32x4 ja[BLK], tk[BLK], tq[BLK];
+#pragma unroll
+                    for (int h = 0; h < BLK; ++h) {
+                        const int kb = s * BLK + h, i0 = 16 * kb + 4 * qd;
+                        const f32x4 sj = *reinterpret_cast<const f32x4 *>(sS16 + x * LDG + i0);
+                        const f32x4 pt = *reinterpret_cast<const f32x4 *>(sP16 + (16 + x) * LDG + i0);
+                        ja[h] = to_f32x4<ET>(frag_row<ET>(sK, LDK, 0, 0, kb, x, qd)) * sj;
+                        tk[h] = to_f32x4<ET>(frag_row<ET>(sK, LDK, 16, 0, kb, x, qd)) * pt;
+                        tq[h] = to_f32x4<ET>(frag_row<ET>(sQ, LDK, 16, 0, kb, x, qd)) * pt;
+                    }
+                    const FR fa = frag_of<ET>(ja);
+                    zk = mfma_step(fa, frag_of<ET>(tk), zk);
+                    zq = mfma_step(fa, frag_of<ET>(tq), zq);
+                }
+                const int t = 16 + x;
+                const float bv = sb[t];
+                st4<ET>(sAn + t * LDC + 4 * qd, cvt4<ET>(zk * (-bv)));
+                st4<ET>(sQKR + t * LDC + 4 * qd, cvt4<ET>(zq * scale));
+            }
+        }
+        // K diag(G), Q diag(G), K diag(G_last / G) and G_last, elementwise
+        for (int it = tid; it < L::GUNITS; it += NT) {
+            const int t = it / (DK / 4), i0 = 4 * (it - t * (DK / 4));
+            const int blk = t >> 4;
+            f32x4 G = *reinterpret_cast<const f32x4 *>(sP16 + t * LDG + i0);
+            f32x4 Rl = *reinterpret_cast<const f32x4 *>(sS16 + t * LDG + i0);
+            if (NBT == 2 && blk == 1) G *= *reinterpret_cast<const f32x4 *>(sBT + i0);
+            if (NBT == 2 && blk == 0) Rl *= *reinterpret_cast<const f32x4 *>(sBT + DK + i0);
+            const f32x4 kf = to_f32x4<ET>(ld4<ET>(sK + t * LDK + i0));
+            const f32x4 qf = to_f32x4<ET>(ld4<ET>(sQ + t * LDK + i0));
+            st4<ET>(sKg + t * LDK + i0, cvt4<ET>(kf * G));
+            st4<ET>(sQg + t * LDK + i0, cvt4<ET>(qf * G));
+            st4<ET>(sKr + t * LDK + i0, cvt4<ET>(kf * Rl));
+            if (t == 0) {
+                f32x4 gl = *reinterpret_cast<const f32x4 *>(sBT + i0);
+                if (NBT == 2) gl *= *reinterpret_cast<const f32x4 *>(sBT + DK + i0);
+                *reinterpret_cast<f32x4 *>(sGl + i0) = gl;
+            }
+        }
+        lds_barrier();
+
+        // ---- (c) X = (K diag G) S0^T and Y^T = S0 (Q diag G)^T for this wave's columns
+        X4 Sf[NBK][NB];
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) Sf[kb][vb] = cvt4<ET>(S[kb][vb]);
+        f32x4 Xa[NBT][NB], Ya[NB][NBT];
+#pragma unroll
+        for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) { Xa[tb][vb] = zero4(); Ya[vb][tb] = zero4(); }
+#pragma unroll
+        for (int s = 0; s < NSK; ++s) {
+            FR fk[NBT], fq[NBT];
+#pragma unroll
+            for (int tb = 0; tb < NBT; ++tb) {
+                fk[tb] = make_frag<ET>(s, NBK, [&](int kb) { return frag_row<ET>(sKg, LDK, 16 * tb, 0, kb, x, qd); });
+                fq[tb] = make_frag<ET>(s, NBK, [&](int kb) { return frag_row<ET>(sQg, LDK, 16 * tb, 0, kb, x, qd); });
+            }
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) {
+                FR fs = make_frag<ET>(s, NBK, [&](int kb) { return Sf[kb][vb]; });
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    Xa[tb][vb] = mfma_step(fk[tb], fs, Xa[tb][vb]);
+                    Ya[vb][tb] = mfma_step(fs, fq[tb], Ya[vb][tb]);
+                }
+            }
+        }
+
+        // ---- (d) D = (I + A)^-1 beta (V - X), blocked forward substitution
+        f32x4 Da[NBT][NB];
+        X4 Df[NBT][NB];
+#pragma unroll
+        for (int ib = 0; ib < NBT; ++ib) {
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + 16 * ib + 4 * qd);
+            f32x4 Z[NB];
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) {
+                const f32x4 vv = to_f32x4<ET>(frag_col<ET>(sV, LDV, 0, vloc + 16 * vb, ib, x, qd));
+                Z[vb] = bv * (vv - Xa[ib][vb]);
+            }
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+                if (s * BLK >= ib) continue;
+                FR fa = make_frag<ET>(s, ib, [&](int jb) { return frag_row<ET>(sAn, LDC, 16 * ib, 0, jb, x, qd); });
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    FR fd = make_frag<ET>(s, ib, [&](int jb) { return Df[jb][vb]; });
+                    Z[vb] = mfma_step(fa, fd, Z[vb]);
+                }
+            }
+            FR ft = make_frag<ET>(0, 1, [&](int) { return frag_row<ET>(sTd, LDT, 16 * ib, 0, 0, x, qd); });
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) {
+                FR fz = make_frag<ET>(0, 1, [&](int) { return cvt4<ET>(Z[vb]); });
+                Da[ib][vb] = mfma_step(ft, fz, zero4());
+                Df[ib][vb] = cvt4<ET>(Da[ib][vb]);
+            }
+        }
+
+        // ---- (e) Y^T = (S0 (Q diag G)^T) / sqrt(Dk) + D^T QKR^T
+#pragma unroll
+        for (int tb = 0; tb < NBT; ++tb) {
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) Ya[vb][tb] *= scale;
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+                if (s * BLK > tb) continue;
+                FR fr = make_frag<ET>(s, NBT, [&](int jb) { return frag_row<ET>(sQKR, LDC, 16 * tb, 0, jb, x, qd); });
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    FR fd = make_frag<ET>(s, NBT, [&](int jb) { return Df[jb][vb]; });
+                    Ya[vb][tb] = mfma_step(fd, fr, Ya[vb][tb]);
+                }
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < NBT; ++tb) {
+            const int t = 16 * tb + x;
+            if (t < cn) {
+                ET *yrow = y + (((size_t)b * T + t0 + t) * Hv + hv) * Dv + vloc + 4 * qd;
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) st4<ET>(yrow + 16 * vb, cvt4<ET>(Ya[vb][tb]));
+            }
+        }
+
+        // ---- (f) S^T <- diag(G_last) S^T + (K diag(G_last / G))^T D
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb) {
+            const f32x4 gl = *reinterpret_cast<const f32x4 *>(sGl + 16 * kb + 4 * qd);
+            FR fk[NST];
+#pragma unroll
+            for (int s = 0; s < NST; ++s)
+                fk[s] = make_frag<ET>(s, NBT, [&](int tb) { return frag_col<ET>(sKr, LDK, 0, 16 * kb, tb, x, qd); });
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) S[kb][vb] *= gl;
+#pragma unroll
+            for (int s = 0; s < NST; ++s) {
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    FR fd = make_frag<ET>(s, NBT, [&](int tb) { return Df[tb][vb]; });
+                    S[kb][vb] = mfma_step(fk[s], fd, S[kb][vb]);
+                }
+            }
+        }
+        if (n + 1 < nchunks) {
+            lds_barrier();                 // chunk n is done with LDS
+            stage(min(C, T - t0 - C));
+        }
+    }
+
+#pragma unroll
+    for (int vb = 0; vb < NB; ++vb) {
+        const size_t row = sbase + (size_t)(vloc + 16 * vb + x) * DK;
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+            *reinterpret_cast<f32x4 *>(state_out + row + 16 * kb + 4 * qd) = S[kb][vb];
+    }
+}
+
+// Chunk length: 32 for 16-bit inputs, 16 for float32 (LDS budget).
+template <typename ET, int DK, int DV>
+hipError_t launch_chunk_vg_dv(const FwdArgs &a, hipStream_t st) {
+    constexpr int NB = DV >= 128 ? 2 : 1;
+    const long nslots = (long)a.B * a.Hv;
+    const int group = a.Hv / a.Hk;
+    const int xcd_group = (group > 1 && nslots % (8L * group) == 0) ? group : 1;
+    auto go = [&](auto cc) -> hipError_t {
+        constexpr int C = decltype(cc)::value;
+        using L = VgCfg<ET, DK, DV, C, NB>;
+        hipLaunchKernelGGL((chunk_vg_kernel<ET, DK, DV, C, NB>), dim3((unsigned)nslots), dim3(L::NT), 0, st,
+                           static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
+                           static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, xcd_group, a.scale, a.flags);
+        return hipGetLastError();
+    };
+    if constexpr (sizeof(ET) == 4) {
+        return go(std::integral_constant<int, 16>{});
+    } else {
+        if (a.C == 16) return go(std::integral_constant<int, 16>{});
+        return go(std::integral_constant<int, 32>{});
+    }
+}
+
+template <typename ET, int DK>
+hipError_t launch_chunk_vg_dk(const FwdArgs &a, hipStream_t st) {
+    switch (a.Dv) {
+    case 32: return launch_chunk_vg_dv<ET, DK, 32>(a, st);
+    case 64: return launch_chunk_vg_dv<ET, DK, 64>(a, st);
+    case 128: return launch_chunk_vg_dv<ET, DK, 128>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename ET>
+hipError_t launch_chunk_vg_typed(const FwdArgs &a, hipStream_t st) {
+    switch (a.Dk) {
+    case 32: return launch_chunk_vg_dk<ET, 32>(a, st);
+    case 64: return launch_chunk_vg_dk<ET, 64>(a, st);
+    case 128: return launch_chunk_vg_dk<ET, 128>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

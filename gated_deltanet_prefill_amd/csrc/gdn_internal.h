@@ -9,6 +9,7 @@ namespace gdn {
 // the C ABI).
 constexpr int kTiledHeads = 1;     // key head of value head hv is hv mod Hk
 constexpr int kLogGate = 2;        // g holds log(decay)
+constexpr int kVectorGate = 4;     // g is [B,T,Hv,Dk]: one decay per key dimension
 
 struct FwdArgs {
     const void *q, *k, *v;
@@ -25,6 +26,10 @@ struct FwdArgs {
 hipError_t launch_chunk_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_f16(const FwdArgs &a, hipStream_t s);
+// the chunked kernel for a decay per key dimension (FwdArgs::flags & kVectorGate)
+hipError_t launch_chunk_vg_f32(const FwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_vg_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_vg_f16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_step(int dtype, const FwdArgs &a, hipStream_t s);
 hipError_t launch_seq(int dtype, const FwdArgs &a, hipStream_t s);
 

@@ -22,7 +22,9 @@ constexpr int kStepLanesPerRow = 8;
 // four value rows per lane
 constexpr long kSeqMinWaves = 2048;
 
-template <typename ET, int DK>
+// VG: g is [B,Hv,Dk], one decay per key dimension (column i of the state
+// decays by g_i); else one decay per (batch, value head).
+template <typename ET, int DK, bool VG>
 __global__ __launch_bounds__(256)
 void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                  const ET *__restrict__ v, const float *__restrict__ g,
@@ -51,6 +53,14 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         qv[m] = to_f32x4<ET>(ld4<ET>(qp + e));
         s[m] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + e) : zero4();
     }
+    if constexpr (VG) {             // decay each key column first: s <- s diag(g)
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+            const f32x4 gv = *reinterpret_cast<const f32x4 *>(g + (size_t)slot * DK + 4 * (m * LPR + sub));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[m][i] *= decay_of(gv[i], flags);
+        }
+    }
     float a = 0.f, bq = 0.f, kq = 0.f;
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
@@ -67,7 +77,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         bq += __shfl_xor(bq, off);
         kq += __shfl_xor(kq, off);
     }
-    const float gt = decay_of(g[slot], flags), bt = beta[slot];
+    const float gt = VG ? 1.f : decay_of(g[slot], flags), bt = beta[slot];
     const float vj = to_f32(v[(size_t)slot * Dv + j]);
     const float d = bt * (vj - gt * a);
 #pragma unroll
@@ -78,15 +88,20 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     if (sub == 0) y[(size_t)slot * Dv + j] = from_f32<ET>((gt * bq + d * kq) * scale);
 }
 
-template <typename ET, int DK>
-static hipError_t launch_step_inst(const FwdArgs &a, hipStream_t st) {
+template <typename ET, int DK, bool VG>
+static hipError_t launch_step_vg(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)a.B * (unsigned)a.Hv * (unsigned)(a.Dv / kStepRowsPerBlock));
     const dim3 block(kStepRowsPerBlock * kStepLanesPerRow);
-    hipLaunchKernelGGL((step_kernel<ET, DK>), grid, block, 0, st,
+    hipLaunchKernelGGL((step_kernel<ET, DK, VG>), grid, block, 0, st,
                        static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                        static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                        static_cast<ET *>(a.y), a.Hk, a.Hv, a.Dv, a.scale, a.flags);
     return hipGetLastError();
+}
+
+template <typename ET, int DK>
+static hipError_t launch_step_inst(const FwdArgs &a, hipStream_t st) {
+    return (a.flags & kVectorGate) ? launch_step_vg<ET, DK, true>(a, st) : launch_step_vg<ET, DK, false>(a, st);
 }
 
 template <typename ET>
@@ -148,7 +163,9 @@ template <typename ET> struct RowVec<ET, 4> {
     static __device__ __forceinline__ float at(T v, int i) { return to_f32(v[i]); }
 };
 
-template <typename ET, int DK, int R>
+// VG: g is [B,T,Hv,Dk]; each token first decays the state's key columns by
+// their own factors (no deferred scale), then runs the same steps.
+template <typename ET, int DK, int R, bool VG>
 __global__ __launch_bounds__(256)
 void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 const ET *__restrict__ v, const float *__restrict__ g,
@@ -169,7 +186,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const ET *kp = k + ((size_t)b * T * Hk + hk) * DK + 4 * sub;
     const ET *qp = q + ((size_t)b * T * Hk + hk) * DK + 4 * sub;
     const ET *vp = v + ((size_t)b * T * Hv + hv) * Dv + j0;
-    const float *gp = g + (size_t)b * T * Hv + hv, *bp = beta + (size_t)b * T * Hv + hv;
+    const float *gp = g + ((size_t)b * T * Hv + hv) * (VG ? DK : 1), *bp = beta + (size_t)b * T * Hv + hv;
     ET *yp = y + ((size_t)b * T * Hv + hv) * Dv + j0;
     const size_t row0 = ((size_t)slot * Dv + j0) * DK + 4 * sub;
 
@@ -183,6 +200,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     typename Vec<ET>::x4 kn[NP], qn[NP];
     typename RV::T vn{};
     float gn = 0.f, bn = 0.f;
+    f32x4 gvn[VG ? NP : 1];
     auto load = [&](int t) {
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
@@ -190,7 +208,13 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             qn[m] = ld4<ET>(qp + (size_t)t * qks + 32 * m);
         }
         vn = RV::ld(vp + (size_t)t * vs);
-        gn = gp[(size_t)t * Hv];
+        if constexpr (VG) {
+#pragma unroll
+            for (int m = 0; m < NP; ++m)
+                gvn[m] = *reinterpret_cast<const f32x4 *>(gp + (size_t)t * Hv * DK + 4 * sub + 32 * m);
+        } else {
+            gn = gp[(size_t)t * Hv];
+        }
         bn = bp[(size_t)t * Hv];
     };
     if (T > 0) load(0);
@@ -203,15 +227,31 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             qv[m] = to_f32x4<ET>(qn[m]);
         }
         const typename RV::T vt = vn;
-        const float gt = decay_of(gn, flags), bt = bn;
+        f32x4 gvt[VG ? NP : 1];
+        if constexpr (VG) {
+#pragma unroll
+            for (int m = 0; m < NP; ++m) gvt[m] = gvn[m];
+        }
+        const float gt = VG ? 1.f : decay_of(gn, flags), bt = bn;
         if (t + 1 < T) load(t + 1);
-        c *= gt;
-        if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the slot
+        if constexpr (VG) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+            for (int m = 0; m < NP; ++m) {
+                f32x4 dm;
 #pragma unroll
-                for (int m = 0; m < NP; ++m) s[r][m] = c * s[r][m];
-            c = 1.f;
+                for (int i = 0; i < 4; ++i) dm[i] = decay_of(gvt[m][i], flags);
+#pragma unroll
+                for (int r = 0; r < R; ++r) s[r][m] *= dm;
+            }
+        } else {
+            c *= gt;
+            if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the slot
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < NP; ++m) s[r][m] = c * s[r][m];
+                c = 1.f;
+            }
         }
         float kq = 0.f, a[R], bq[R];
 #pragma unroll
@@ -228,7 +268,7 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         kq = sum8(kq);
-        const float rc = __builtin_amdgcn_rcpf(c);   // 1 ulp
+        const float rc = VG ? 1.f : __builtin_amdgcn_rcpf(c);   // 1 ulp
         float yo[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -252,14 +292,19 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             *reinterpret_cast<f32x4 *>(state_out + row0 + (size_t)r * DK + 32 * m) = c * s[r][m];
 }
 
-template <typename ET, int DK, int R>
-static hipError_t launch_seq_inst(const FwdArgs &a, hipStream_t st) {
+template <typename ET, int DK, int R, bool VG>
+static hipError_t launch_seq_vg(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)a.B * (unsigned)a.Hv * (unsigned)(a.Dv / (32 * R)));
-    hipLaunchKernelGGL((seq_kernel<ET, DK, R>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((seq_kernel<ET, DK, R, VG>), grid, dim3(256), 0, st,
                        static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                        static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                        static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, a.scale, a.flags);
     return hipGetLastError();
+}
+
+template <typename ET, int DK, int R>
+static hipError_t launch_seq_inst(const FwdArgs &a, hipStream_t st) {
+    return (a.flags & kVectorGate) ? launch_seq_vg<ET, DK, R, true>(a, st) : launch_seq_vg<ET, DK, R, false>(a, st);
 }
 
 // rows per lane: R = 4 when the grid has enough waves to fill the chip,

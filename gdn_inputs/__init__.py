@@ -164,6 +164,29 @@ def make_inputs(B, T, Hk, Hv, Dk, Dv, dtype="bf16", *, gate="softplus",
     return out
 
 
+def vector_gate(B, T, Hv, Dk, *, seed=0, kind="sigmoid"):
+    """A decay per key dimension, float32 [B,T,Hv,Dk] (seeded).
+
+    ``sigmoid``: sigmoid(N(0,1) + 2) per entry (mean about 0.85, some
+    entries near 0.3); ``near_one``: U[0.95, 1), the slow decays of long
+    contexts; ``mixed``: half the key dimensions near 1, half small
+    (U[0.05, 0.5]), so that some columns of the state are forgotten within a
+    few tokens while others persist.
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "sigmoid":
+        g = _sigmoid(rng.standard_normal((B, T, Hv, Dk)) + 2.0)
+    elif kind == "near_one":
+        g = 0.95 + 0.05 * rng.random((B, T, Hv, Dk))
+    elif kind == "mixed":
+        g = 0.95 + 0.05 * rng.random((B, T, Hv, Dk))
+        small = rng.random(Dk) < 0.5
+        g[..., small] = 0.05 + 0.45 * rng.random((B, T, Hv, int(small.sum())))
+    else:
+        raise ValueError(f"unknown vector gate {kind!r}")
+    return g.astype(np.float32)
+
+
 def workload_inputs(name: str, *, seed=0, gate=None, **overrides):
     """Inputs of one named workload (see ``WORKLOADS``)."""
     cfg = dict(WORKLOADS[name])

@@ -53,7 +53,7 @@ enum {
     GDN_ERR_SHAPE = -2,       /* negative size, or Hv not a multiple of Hk   */
     GDN_ERR_UNSUPPORTED = -3, /* Dk, Dv, C or flags outside the supported set */
     GDN_ERR_ALIAS = -4,       /* an output overlaps another buffer           */
-    GDN_ERR_ALIGN = -5,       /* a pointer is not 16-byte (4 for g, beta) aligned */
+    GDN_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned (4 for beta and a scalar g) */
     GDN_ERR_HIP = -6,         /* a HIP launch failed                         */
     GDN_ERR_DTYPE = -7        /* dtype is not a gdn_dtype value              */
 };
@@ -148,14 +148,24 @@ int gdn_step(const void *q, const void *k, const void *v,
  *                     instead of hv / (Hv/Hk) (the grouped map).
  *   GDN_GATE_LOG      g holds log(decay); the decay used is exp(g), so g = 0
  *                     keeps the state and g = -inf forgets it.
+ *   GDN_GATE_VECTOR   g holds one decay per key dimension: [B,T,Hv,Dk]
+ *                     float32 ([B,Hv,Dk] for gdn_step_ex), 16-byte aligned.
+ *                     Key column i of the state decays by g_t[i]:
+ *                       S_t = S_{t-1} diag(g_t) (I - beta_t k_t k_t^T)
+ *                             + beta_t v_t k_t^T
+ *                     (the 4-D "vector" gate the MLX pull request page names
+ *                     as a shape its kernels would misread).  The chunked
+ *                     path then uses chunks of at most 32 tokens (16 for
+ *                     float32 inputs) whatever C asks for.
  *
- * flags = 0 is exactly gdn_chunk_fwd / gdn_seq_fwd / gdn_step.  Any other
- * bit is GDN_ERR_UNSUPPORTED.  All other arguments, layouts, alignment,
+ * flags = 0 is exactly gdn_chunk_fwd / gdn_seq_fwd / gdn_step; the bits
+ * combine freely.  Any other bit is GDN_ERR_UNSUPPORTED.  All other arguments, layouts, alignment,
  * aliasing and errors as for the entry points without _ex.
  */
 enum {
     GDN_HEADS_TILED = 1,
-    GDN_GATE_LOG = 2
+    GDN_GATE_LOG = 2,
+    GDN_GATE_VECTOR = 4
 };
 
 int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v,

@@ -141,7 +141,7 @@ def test_ex_flags(lib):
     """Unknown flag bits are rejected; known ones pass the host checks (B = 0
     stops before any launch); the _ex calls check arguments like the plain
     ones."""
-    for bad in (4, 8, 1 << 30, -1):
+    for bad in (8, 16, 1 << 30, -1):
         assert chunk_ex(lib, bad) == UNSUP
         assert lib.gdn_seq_fwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A),
                                   P(8 * A), 1, 4, 1, 1, 32, 32, bad, 1, None) == UNSUP
@@ -152,3 +152,18 @@ def test_ex_flags(lib):
         assert chunk_ex(lib, good, Hk=2, Hv=3) == SHAPE
         assert chunk_ex(lib, good, C=8) == UNSUP
         assert chunk_ex(lib, good, y=2 * A) == ALIAS
+
+
+def test_vector_gate_checks(lib):
+    """A per-key-dimension gate (flag 4) is [B,T,Hv,Dk] and 16-byte aligned:
+    the alignment and overlap checks use that size."""
+    VEC = 4
+    assert chunk_ex(lib, VEC, g=4 * A + 4) == ALIGN
+    # a scalar gate needs 4 bytes only: the call gets past the pointer
+    # checks and stops at the (invalid) chunk length, before any launch
+    assert chunk_ex(lib, 0, g=4 * A + 4, C=8) == UNSUP
+    # y 256 bytes after g: clear of a scalar gate (16 bytes), inside a vector one (512)
+    assert chunk_ex(lib, VEC, y=4 * A + 256) == ALIAS
+    assert chunk_ex(lib, 0, y=4 * A + 256, C=8) == UNSUP
+    assert lib.gdn_step_ex(P(A), P(2 * A), P(3 * A), P(4 * A + 4), P(5 * A), P(6 * A), P(7 * A),
+                           P(8 * A), 1, 1, 1, 32, 32, VEC, 1, None) == ALIGN

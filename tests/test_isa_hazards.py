@@ -107,7 +107,8 @@ def test_scan_finds_a_planted_chain():
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_no_close_mixed_shape_accumulator_chains():
-    srcs = ["gdn_chunk_bf16.hip", "gdn_chunk_f16.hip", "gdn_chunk_f32.hip"]
+    srcs = ["gdn_chunk_bf16.hip", "gdn_chunk_f16.hip", "gdn_chunk_f32.hip",
+            "gdn_chunk_vg_bf16.hip", "gdn_chunk_vg_f16.hip", "gdn_chunk_vg_f32.hip"]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         asms = list(ex.map(_compile, srcs))
     bad = [(src, k[:70], s, p, c) for src, asm in zip(srcs, asms)
