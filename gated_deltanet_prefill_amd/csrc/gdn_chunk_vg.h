@@ -53,7 +53,11 @@ struct VgCfg : ChunkCfg<ET, DK_, DVS_, C_, NB_> {
     static constexpr int oKg = oGl + DK_ * 4;             // K diag(G)       [C][LDK]
     static constexpr int oQg = oKg + C_ * Base::LDK * Base::ES;   // Q diag(G)
     static constexpr int oKr = oQg + C_ * Base::LDK * Base::ES;   // K diag(G_last / G)
-    static constexpr int VBYTES = oKr + C_ * Base::LDK * Base::ES;
+    static constexpr int oPart = oKr + C_ * Base::LDK * Base::ES;  // per-wave partial tiles
+    static constexpr int VBYTES = oPart + Base::NW * 2 * 64 * 16;
+    // the diagonal tiles of one block are summed over NPART waves, each
+    // taking an equal share of the key steps
+    static constexpr int NPART_ = Base::NW / Base::NBT;
     static constexpr int GUNITS = C_ * DK_ / 4;           // 16-byte units of a chunk's gates
     static constexpr int PERG = (GUNITS + Base::NT - 1) / Base::NT;
     static_assert(VBYTES <= 160 * 1024, "LDS budget");
@@ -143,6 +147,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                   LDT = L::LDT, LDG = L::LDG, EPU = L::EPU;
     constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
     constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
+    constexpr int NPART_V = L::NPART_;
     static_assert(NBK % BLK == 0, "whole key steps");
 
     __shared__ __attribute__((aligned(16))) char smem[L::VBYTES];
@@ -287,16 +292,21 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (n + 1 < nchunks) prefetch(t0 + C);
         lds_barrier();                     // chunk n staged
 
-        // ---- (a) wave w < NBT: the scans of block w (P16, S16, block
-        // totals) and its diagonal tiles of K K^T and Q K^T, one product per
-        // level; lane x of each DPP row is token 16 w + x.
-        if (wave < NBT) {
-            const int bt = wave, t = 16 * bt + x;
+        // ---- (a) wave w: block w % NBT over its share of the key steps:
+        // the scans (P16, S16, block totals) and the partial diagonal tiles
+        // of K K^T and Q K^T, one product per level, reduced to this lane's
+        // entries (lane x of each DPP row is token 16 bt + x; the tile lane
+        // (x, qd) holds column t = 16 bt + x, rows j = 16 bt + 4 qd + r).
+        constexpr int NPART = NPART_V < NSK ? NPART_V : NSK;
+        constexpr int SPP = NSK / NPART;                 // key steps per wave
+        if (wave < NBT * NPART) {
+            const int bt = wave % NBT, part = wave / NBT, t = 16 * bt + x;
             f32x4 kk[4], qk[4], q0 = zero4();
 #pragma unroll
             for (int m = 0; m < 4; ++m) { kk[m] = zero4(); qk[m] = zero4(); }
 #pragma unroll
-            for (int s = 0; s < NSK; ++s) {
+            for (int ss = 0; ss < SPP; ++ss) {
+                const int s = part * SPP + ss;
                 f32x4 ka[4][BLK], kl[4][BLK], ql[4][BLK], k0[BLK], qq[BLK];
 #pragma unroll
                 for (int h = 0; h < BLK; ++h) {
@@ -331,59 +341,46 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
                 q0 = mfma_step(frag_of<ET>(k0), frag_of<ET>(qq), q0);
             }
-            // lane (x, qd) holds column t = 16 bt + x, rows j = 16 bt + 4 qd + r
-            const float bv = sb[t];
-            f32x4 a, o;
+            // keep each entry's own level (the highest bit in which the
+            // in-block indices of t and j differ): a weighted sum, no branches
+            f32x4 za, zo;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int jl = 4 * qd + r, d = jl ^ x;
-                const int m = d >= 8 ? 3 : d >= 4 ? 2 : d >= 2 ? 1 : 0;
-                const float zk = m == 3 ? kk[3][r] : m == 2 ? kk[2][r] : m == 1 ? kk[1][r] : kk[0][r];
-                const float zq = m == 3 ? qk[3][r] : m == 2 ? qk[2][r] : m == 1 ? qk[1][r] : qk[0][r];
-                a[r] = (jl < x) ? bv * zk : 0.f;
-                o[r] = (jl < x) ? scale * zq : (jl == x) ? scale * q0[r] : 0.f;
+                const float w3 = d >= 8 ? 1.f : 0.f, w2 = (d >= 4 && d < 8) ? 1.f : 0.f,
+                            w1 = (d >= 2 && d < 4) ? 1.f : 0.f, w0 = d == 1 ? 1.f : 0.f;
+                const float lower = jl < x ? 1.f : 0.f, diag = jl == x ? 1.f : 0.f;
+                za[r] = lower * (w0 * kk[0][r] + w1 * kk[1][r] + w2 * kk[2][r] + w3 * kk[3][r]);
+                zo[r] = lower * (w0 * qk[0][r] + w1 * qk[1][r] + w2 * qk[2][r] + w3 * qk[3][r]) +
+                        diag * q0[r];
             }
+            f32x4 *part_out = reinterpret_cast<f32x4 *>(smem + L::oPart) + (wave * 2) * 64 + lane;
+            part_out[0] = za;
+            part_out[64] = zo;
+        }
+        lds_barrier();
+
+        // ---- (b) waves w < NBT: the sum of block w's partial tiles, times
+        // beta (A) and 1/sqrt(Dk) (QKR)
+        if (wave < NBT) {
+            const int bt = wave, t = 16 * bt + x;
+            f32x4 a = zero4(), o = zero4();
+#pragma unroll
+            for (int pp = 0; pp < NPART; ++pp) {
+                const f32x4 *pin = reinterpret_cast<const f32x4 *>(smem + L::oPart) + ((bt + NBT * pp) * 2) * 64 + lane;
+                a += pin[0];
+                o += pin[64];
+            }
+            a *= sb[t];
+            o *= scale;
             const int j0 = 16 * bt + 4 * qd;
             st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
             st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
             *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
         }
-        lds_barrier();
-
-        // ---- (b) diagonal inverses (waves < NBT); the tile between the two
-        // blocks (one more wave); the scaled K and Q for the state products
-        // and the update (every thread).
-        if (wave < NBT) {
-            const int base = 16 * wave;
-            const int p = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
-            f32x4 arow[4][4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4)
-                    arow[m][j4] = *reinterpret_cast<const f32x4 *>(sAd + (base + p + 4 * m) * LDD + 4 * j4);
-            float s[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) s[m] = (p + 4 * m == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < 15; ++j) {
-                float xj;
-                switch (j & 3) {
-                case 0: xj = quad_bcast<0>(s[j >> 2]); break;
-                case 1: xj = quad_bcast<1>(s[j >> 2]); break;
-                case 2: xj = quad_bcast<2>(s[j >> 2]); break;
-                default: xj = quad_bcast<3>(s[j >> 2]); break;
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
-        }
         if constexpr (NBT == 2) {
             // tokens j in block 0, t in block 1: R = P16_t S16_j
-            if (wave == (NW > NBT ? NBT : 0)) {
+            if (wave == NW - 1) {
                 f32x4 zk = zero4(), zq = zero4();
 #pragma unroll
                 for (int s = 0; s < NSK; ++s) {
@@ -428,6 +425,36 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         }
         lds_barrier();
 
+        // ---- (c) diagonal inverses (waves < NBT)
+        if (wave < NBT) {
+            const int base = 16 * wave;
+            const int p = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
+            f32x4 arow[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4)
+                    arow[m][j4] = *reinterpret_cast<const f32x4 *>(sAd + (base + p + 4 * m) * LDD + 4 * j4);
+            float s[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) s[m] = (p + 4 * m == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) {
+                float xj;
+                switch (j & 3) {
+                case 0: xj = quad_bcast<0>(s[j >> 2]); break;
+                case 1: xj = quad_bcast<1>(s[j >> 2]); break;
+                case 2: xj = quad_bcast<2>(s[j >> 2]); break;
+                default: xj = quad_bcast<3>(s[j >> 2]); break;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
+        }
+
         // ---- (c) X = (K diag G) S0^T and Y^T = S0 (Q diag G)^T for this wave's columns
         X4 Sf[NBK][NB];
 #pragma unroll
@@ -457,6 +484,8 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         }
+
+        lds_barrier();                     // the inverses are in LDS
 
         // ---- (d) D = (I + A)^-1 beta (V - X), blocked forward substitution
         f32x4 Da[NBT][NB];
