@@ -57,7 +57,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, TFLOP/s
 PREFILL = dict(B=8, T=8192, Hk=16, Hv=32, Dk=128, Dv=128, C=64, dtype="bf16")
 DECODE = dict(B=64, T=256, Hk=16, Hv=32, Dk=128, Dv=128, dtype="f16")
-CHUNK_KERNEL_SOURCES = ["gdn_chunk_pipe.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h",
+CHUNK_KERNEL_SOURCES = ["gdn_chunk_pipe.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_internal.h",
                         "gdn_device.h", "gdn_chunk_bf16.hip"]
 # the kernel that runs the long-prefill workload (bf16, Dk = Dv = 128, C = 64)
 CHUNK_KERNEL = "chunk_pipe_kernel"
