@@ -65,11 +65,13 @@ struct VgCfg : ChunkCfg<ET, DK_, DVS_, C_, NB_> {
 };
 
 // Products over aligned segments of the sixteen tokens of a block, one token
-// per lane of a DPP row (x = lane index in the row).  Segment sizes 2, 4, 8
-// and 16; "prefix" includes the lane's own token, "after" excludes it.
+// per lane of a DPP row (x = lane index in the row), for the four key
+// dimensions a lane holds.  p[m]: product over the lane's aligned 2^m-token
+// segment up to and including the lane; e[m]: product over that segment
+// after the lane (m = 0..4; p[0] = g, e[0] = 1).
 struct SegScan {
-    float p[5];       // p[m]: product over the lane's 2^m segment up to and including it
-    float e[5];       // e[m]: product over the lane's 2^m segment after it
+    f32x4 p[5];
+    f32x4 e[5];
 };
 
 template <int CTRL>
@@ -78,45 +80,43 @@ __device__ __forceinline__ float dpp_keep(float v) {   // DPP move, 1 where no s
         __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
+// The same DPP move on each of the four components (independent chains).
+template <typename F>
+__device__ __forceinline__ f32x4 each4(f32x4 v, F f) {
+    return f32x4{f(v[0]), f(v[1]), f(v[2]), f(v[3])};
+}
+
 // Every cross-lane move below is issued by all sixteen lanes before any
 // lane-dependent choice: a DPP move inside a branch would read lanes the
 // branch has switched off.
-__device__ __forceinline__ SegScan seg_scan(float g, int x) {
+__device__ __forceinline__ SegScan seg_scan(f32x4 g, int x) {
+    const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+    auto sel = [](bool c, f32x4 a, f32x4 b) { return c ? a : b; };
     SegScan r;
-    // inclusive prefix: upper halves multiply by the total of their lower half
-    const float p0 = g;
-    const float a1 = dpp_row_shr<1>(p0);
-    const float p1 = (x & 1) ? p0 * a1 : p0;
-    const float a2 = quad_bcast<1>(p1);
-    const float p2 = (x & 2) ? p1 * a2 : p1;
-    const float a3 = dpp_row_shr<4>(quad_bcast<3>(p2));           // lower quad's total, one quad up
-    const float p3 = (x & 4) ? p2 * a3 : p2;
-    const float w3 = quad_bcast<3>(p3);
-    const float w3a = dpp_row_shr<4>(w3);
-    const float w3b = dpp_row_shr<4>(w3a);                        // lanes 8-11 / 12-15 get lane 7's
-    const float p4 = (x & 8) ? p3 * ((x & 4) ? w3b : w3a) : p3;
-    // inclusive suffix: lower halves multiply by the total of their upper half
-    const float s0 = g;
-    const float b1 = dpp_row_shl<1>(s0);
-    const float s1 = (x & 1) ? s0 : s0 * b1;
-    const float b2 = quad_bcast<2>(s1);
-    const float s2 = (x & 2) ? s1 : s1 * b2;
-    const float b3 = dpp_row_shl<4>(quad_bcast<0>(s2));           // upper quad's total, one quad down
-    const float s3 = (x & 4) ? s2 : s2 * b3;
-    const float v3 = quad_bcast<0>(s3);
-    const float v3a = dpp_row_shl<4>(v3);
-    const float v3b = dpp_row_shl<4>(v3a);                        // lanes 4-7 / 0-3 get lane 8's
-    const float s4 = (x & 8) ? s3 : s3 * ((x & 4) ? v3a : v3b);
+    // prefix: the upper half of each segment multiplies by its lower half's total
+    const f32x4 p0 = g;
+    const f32x4 a1 = each4(p0, [](float v) { return dpp_row_shr<1>(v); });
+    const f32x4 p1 = sel(x & 1, p0 * a1, p0);
+    const f32x4 a2 = each4(p1, [](float v) { return quad_bcast<1>(v); });
+    const f32x4 p2 = sel(x & 2, p1 * a2, p1);
+    const f32x4 a3 = each4(p2, [](float v) { return dpp_row_shr<4>(quad_bcast<3>(v)); });
+    const f32x4 p3 = sel(x & 4, p2 * a3, p2);
+    const f32x4 w3a = each4(p3, [](float v) { return dpp_row_shr<4>(quad_bcast<3>(v)); });
+    const f32x4 w3b = each4(w3a, [](float v) { return dpp_row_shr<4>(v); });   // lane 7's, two quads up
+    const f32x4 p4 = sel(x & 8, p3 * sel(x & 4, w3b, w3a), p3);
+    // after the lane: the lower half of each segment multiplies by its upper
+    // half's total; s = g e is the product from the lane to the segment's end
+    const f32x4 b1 = each4(g, [](float v) { return dpp_keep<0x101>(v); });      // next lane's g
+    const f32x4 e1 = sel(x & 1, one, b1);
+    const f32x4 b2 = each4(g * e1, [](float v) { return quad_bcast<2>(v); });
+    const f32x4 e2 = sel(x & 2, e1, e1 * b2);
+    const f32x4 b3 = each4(g * e2, [](float v) { return dpp_row_shl<4>(quad_bcast<0>(v)); });
+    const f32x4 e3 = sel(x & 4, e2, e2 * b3);
+    const f32x4 v3a = each4(g * e3, [](float v) { return dpp_row_shl<4>(quad_bcast<0>(v)); });
+    const f32x4 v3b = each4(v3a, [](float v) { return dpp_row_shl<4>(v); });   // lane 8's, two quads down
+    const f32x4 e4 = sel(x & 8, e3, e3 * sel(x & 4, v3a, v3b));
     r.p[0] = p0; r.p[1] = p1; r.p[2] = p2; r.p[3] = p3; r.p[4] = p4;
-    // exclusive suffix: the next lane's inclusive suffix when it is in the
-    // same segment, else the empty product
-    const float n1 = dpp_keep<0x101>(s1), n2 = dpp_keep<0x101>(s2),
-                n3 = dpp_keep<0x101>(s3), n4 = dpp_keep<0x101>(s4);
-    r.e[0] = 1.f;
-    r.e[1] = ((x + 1) & 1) ? n1 : 1.f;
-    r.e[2] = ((x + 1) & 3) ? n2 : 1.f;
-    r.e[3] = ((x + 1) & 7) ? n3 : 1.f;
-    r.e[4] = ((x + 1) & 15) ? n4 : 1.f;
+    r.e[0] = one; r.e[1] = e1; r.e[2] = e2; r.e[3] = e3; r.e[4] = e4;
     return r;
 }
 
@@ -314,19 +314,14 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGv + t * LDG + i0);
                     const f32x4 kf = to_f32x4<ET>(frag_row<ET>(sK, LDK, 16 * bt, 0, kb, x, qd));
                     const f32x4 qf = to_f32x4<ET>(frag_row<ET>(sQ, LDK, 16 * bt, 0, kb, x, qd));
-                    f32x4 p16, s16;
+                    const SegScan sc = seg_scan(g4, x);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const SegScan sc = seg_scan(g4[e], x);
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            ka[m][h][e] = kf[e] * sc.e[m];
-                            kl[m][h][e] = kf[e] * sc.p[m];
-                            ql[m][h][e] = qf[e] * sc.p[m];
-                        }
-                        p16[e] = sc.p[4];
-                        s16[e] = sc.e[4];
+                    for (int m = 0; m < 4; ++m) {
+                        ka[m][h] = kf * sc.e[m];
+                        kl[m][h] = kf * sc.p[m];
+                        ql[m][h] = qf * sc.p[m];
                     }
+                    const f32x4 p16 = sc.p[4], s16 = sc.e[4];
                     k0[h] = kf;
                     qq[h] = qf;
                     *reinterpret_cast<f32x4 *>(sP16 + t * LDG + i0) = p16;
@@ -405,7 +400,10 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
         }
         // K diag(G), Q diag(G), K diag(G_last / G) and G_last, elementwise
-        for (int it = tid; it < L::GUNITS; it += NT) {
+#pragma unroll
+        for (int ii = 0; ii < L::PERG; ++ii) {
+            const int it = tid + ii * NT;
+            if (L::GUNITS % NT != 0 && it >= L::GUNITS) break;
             const int t = it / (DK / 4), i0 = 4 * (it - t * (DK / 4));
             const int blk = t >> 4;
             f32x4 G = *reinterpret_cast<const f32x4 *>(sP16 + t * LDG + i0);
