@@ -181,6 +181,31 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// y rows t0 .. t0 + cn - 1 of one slot from accumulator tiles Ya[vb][tb]
+// (lane (x, qd): token 16 tb + x, values vloc + 16 vb + 4 qd + (0..3)),
+// through a buffer resource that spans the cn valid rows: the hardware drops
+// the stores of rows past the end, with no branch around them.  `ybase`
+// points at row t0, `ld` is the row stride in elements.
+template <typename ET, int NB, int NBT>
+__device__ __forceinline__ void store_y(ET *ybase, int ld, int cn, int vloc, int x, int qd,
+                                        const f32x4 (&Ya)[NB][NBT]) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const unsigned rowb = (unsigned)ld * (unsigned)sizeof(ET);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)ybase, (short)0, (int)((unsigned)cn * rowb), 0x00020000);
+#pragma unroll
+    for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) {
+            const int off = (int)((16 * tb + x) * rowb + (vloc + 16 * vb + 4 * qd) * sizeof(ET));
+            if constexpr (sizeof(ET) == 2)
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, cvt4<ET>(Ya[vb][tb])), yr, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, Ya[vb][tb]), yr, off, 0, 0);
+        }
+}
+
 template <typename ET, int DK, int DVS, int C, int NB>
 __global__ __launch_bounds__(4 * DVS / NB, 1)
 void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
@@ -578,15 +603,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         }
 
         // ---- y store: lane holds token t = 16 tb + x, values 16 vb + 4 qd + (0..3)
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-            const int t = 16 * tb + x;
-            if (t < cn) {
-                ET *yrow = y + (((size_t)b * T + t0 + t) * Hv + hv) * Dv + vs * DVS + vloc + 4 * qd;
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) st4<ET>(yrow + 16 * vb, cvt4<ET>(Ya[vb][tb]));
-            }
-        }
+        store_y(y + (((size_t)b * T + t0) * Hv + hv) * Dv + vs * DVS, Hv * Dv, cn, vloc, x, qd, Ya);
 
         // ---- S^T <- G_last S^T + K^T diag(R[c-1][:]) D
         X4 Dpf[NBT][NB];

@@ -532,15 +532,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         }
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-            const int t = 16 * tb + x;
-            if (t < cn) {
-                ET *yrow = y + (((size_t)b * T + t0 + t) * Hv + hv) * Dv + vloc + 4 * qd;
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) st4<ET>(yrow + 16 * vb, cvt4<ET>(Ya[vb][tb]));
-            }
-        }
+        store_y(y + (((size_t)b * T + t0) * Hv + hv) * Dv, Hv * Dv, cn, vloc, x, qd, Ya);
 
         // ---- (f) S^T <- diag(G_last) S^T + (K diag(G_last / G))^T D
 #pragma unroll
