@@ -21,6 +21,9 @@ printed with:
 * ``decode``      256 chained ``gdn_step`` launches on the decode workload
                   (B=64, Hk=16, Hv=32, Dk=Dv=128, fp16 I/O, f32 state in
                   place): state GB/s and total GB/s against 8 TB/s;
+* ``vector_gate`` the long prefill with a decay per key dimension (g
+                  [B,T,Hv,Dk], seeded U[0.95, 1) on the device): launch time
+                  of the vector-gate chunk kernel (C = 32) and its HBM rate;
 * ``multi_token`` T = 2, 4, 8 tokens per call on the decode shapes: the
                   sequential kernel (``gdn_seq_fwd``), the chunked kernel at
                   C = 16 and the library's own choice (C = 0), each call
@@ -181,6 +184,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-multi", action="store_true")
+    ap.add_argument("--no-vector-gate", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args()
@@ -281,6 +285,36 @@ def main():
             "algorithmic_flops_per_launch": nflops,
         },
     }
+    # ---------------- the long prefill with a decay per key dimension
+    if not args.no_vector_gate:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        gvec = 0.95 + 0.05 * torch.rand((P["B"], P["T"], P["Hv"], P["Dk"]), generator=gen, device=dev)
+        s_vg = torch.empty_like(s_in)
+        call = lambda: gdn.chunk_fwd(q, k, v, gvec, beta, s_in, C=32, state_out=s_vg, y=y, stream=stream)
+        call()
+        torch.cuda.synchronize()
+        n = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_vg = e0.elapsed_time(e1) * 1e3 / n
+        vg_bytes = prefill_bytes(**P) + 4 * P["B"] * P["T"] * P["Hv"] * (P["Dk"] - 1)
+        out["vector_gate"] = {
+            "workload": "long prefill with a decay per key dimension (g [B,T,Hv,Dk] f32, U[0.95,1))",
+            "kernel": "chunk_vg_kernel<bf16,128,128,32>", "C": 32,
+            "us_per_launch": us_vg, "tokens_per_s": P["B"] * P["T"] / (us_vg * 1e-6),
+            "hbm_GBps": vg_bytes / (us_vg * 1e-6) / 1e9,
+            "hbm_frac": vg_bytes / (us_vg * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "vs_scalar_gate": us_vg / out["roofline"]["launch_us_avg"],
+            "bytes_per_launch": vg_bytes,
+        }
+        del gvec, s_vg
+        torch.cuda.empty_cache()
+
     del q, k, v, g, beta, y, s_out
     torch.cuda.empty_cache()
 
