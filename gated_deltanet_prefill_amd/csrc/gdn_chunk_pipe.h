@@ -88,8 +88,8 @@ struct PipeCfg {
     static constexpr unsigned oTU = oTW + C * LDTT * 2;  // [C][LDTT]
     static constexpr unsigned NV = 7 * C;                // floats per gate-vector set
     static constexpr unsigned oVec = oTU + C * LDTT * 2; // 3 x gate vectors
-    static constexpr unsigned oGB = oVec + 3 * NV * 4;   // g, beta of the next chunk, as loaded
-    static constexpr unsigned BYTES = oGB + 2 * C * 4;
+    static constexpr unsigned oGB = oVec + 3 * NV * 4;   // g, beta of two chunks, as loaded
+    static constexpr unsigned BYTES = oGB + 2 * 2 * C * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -269,8 +269,9 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             const int t0 = c * C;
             const unsigned off = 4 * (unsigned)(min(lane, T - t0 - 1) * Hv);
             const float *gc = gbase + (size_t)t0 * Hv, *bc = bbase + (size_t)t0 * Hv;
-            const unsigned lg = __builtin_amdgcn_readfirstlane(lds_base + L::oGB);
-            const unsigned lb = __builtin_amdgcn_readfirstlane(lds_base + L::oGB + C * 4);
+            const unsigned gbo = L::oGB + (unsigned)(c & 1) * 2 * C * 4;
+            const unsigned lg = __builtin_amdgcn_readfirstlane(lds_base + gbo);
+            const unsigned lb = __builtin_amdgcn_readfirstlane(lds_base + gbo + C * 4);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
             asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
@@ -285,11 +286,14 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // products P and the inclusive suffix products by four doubling steps;
     // the exclusive suffix Sfx; block totals; G[t] = P[t] x totals of the
     // earlier blocks; Rl[t] = Sfx[t] x totals of the later blocks.
-    auto scan_gates = [&](int c) {
+    // `wait`: the loads of chunk c may still be in flight (else they were
+    // awaited before an earlier barrier).
+    auto scan_gates = [&](int c, bool wait) {
         if (w == 0) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            const float rg = reinterpret_cast<const float *>(smem + L::oGB)[lane];
-            const float rb = reinterpret_cast<const float *>(smem + L::oGB)[C + lane];
+            if (wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const float *gb = reinterpret_cast<const float *>(smem + L::oGB + (c & 1) * 2 * C * 4);
+            const float rg = gb[lane];
+            const float rb = gb[C + lane];
             const int cn = min(C, T - c * C);
             float *gv = Gv(c % 3);
             const float gt = lane < cn ? decay_of(rg, flags) : 1.f;
@@ -378,6 +382,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             issue_k(0);
             issue_q(0);
         }
+        if (nchunks > 1) load_gb(1);                 // awaited before the first barrier
 #pragma unroll
         for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
@@ -394,15 +399,16 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // K, g and beta of chunk n+2 and V of chunk n+1, all awaited before the
         // phase-a barrier (V is read in phase b, K and the gate products by the
         // prep waves next chunk)
+        // The gates are loaded one chunk earlier than K (two buffers), so the
+        // scan of chunk n+2 at the end of phase a reads loads that completed
+        // before the previous barrier instead of waiting for this phase's.
         auto issue_inputs = [&](int n) {
-            if (n + 2 < nchunks) {
-                issue_k(n + 2);
-                load_gb(n + 2);
-            }
+            if (n + 2 < nchunks) issue_k(n + 2);
+            if (n + 3 < nchunks) load_gb(n + 3);
             if (n + 1 < nchunks) issue_v(n + 1);
         };
         auto end_phase_a = [&](int n) {
-            if (n + 2 < nchunks) scan_gates(n + 2);
+            if (n + 2 < nchunks) scan_gates(n + 2, false);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         };
@@ -545,7 +551,7 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         if (nchunks > 0) {
             // gates of chunk 0 (its V comes in the first iteration)
             load_gb(0);
-            scan_gates(0);
+            scan_gates(0, true);
         }
         zero_qkr();
         lds_barrier();
@@ -576,6 +582,22 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     tj[i] = (kJB >> (6 * p + 2 * i)) & 3;
                     tt[i] = (kTB >> (6 * p + 2 * i)) & 3;
                     tq[i] = (kQB >> (3 * p + i)) & 1;
+                }
+                // gate values of the apply steps below, read before the tile
+                // products so that their LDS latency overlaps them
+                const int td = 16 * p + x;
+                const float dg_b = gv[kVb * C + td];
+                const float dg_g = gv[kVg * C + td];
+                const f32x4 dg_g4 = *reinterpret_cast<const f32x4 *>(gv + kVg * C + 16 * p + 4 * qd);
+                const f32x4 od_tot = *reinterpret_cast<const f32x4 *>(gv + kVBT * C);
+                float od_P[3], od_b[3];
+                f32x4 od_S[3];
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const int t = 16 * tt[i] + x;
+                    od_P[i] = gv[kVP * C + t];
+                    od_b[i] = gv[kVb * C + t];
+                    od_S[i] = *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * tj[i] + 4 * qd);
                 }
                 f32x4 acc[5];
 #pragma unroll
@@ -622,14 +644,14 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 // h = product of g over local indices [4 qd + 4, x] by an
                 // inclusive scan along the 16 lanes x of a DPP row.
                 {
-                    const int t = 16 * p + x;
-                    const float bt = gv[kVb * C + t];
-                    float h = (x >= 4 * qd + 4) ? gv[kVg * C + t] : 1.f;
+                    const int t = td;
+                    const float bt = dg_b;
+                    float h = (x >= 4 * qd + 4) ? dg_g : 1.f;
                     h *= dpp_row_shr<1>(h);
                     h *= dpp_row_shr<2>(h);
                     h *= dpp_row_shr<4>(h);
                     h *= dpp_row_shr<8>(h);
-                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gv + kVg * C + 16 * p + 4 * qd);
+                    const f32x4 g4 = dg_g4;
                     f32x4 R;
                     R[3] = h;
                     R[2] = (4 * qd + 3 <= x) ? R[3] * g4[3] : 1.f;
@@ -649,17 +671,17 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 // ---- tiles below the diagonal: R[t][j] = P[t] x (totals of the
                 // blocks strictly between) x Sfx[j]
                 {
-                    const f32x4 tot = *reinterpret_cast<const f32x4 *>(gv + kVBT * C);
+                    const f32x4 tot = od_tot;
 #pragma unroll
                     for (int i = 0; i < 3; ++i) {
-                        const int jb = tj[i], tb = tt[i], t = 16 * tb + x;
-                        float mf = gv[kVP * C + t];
+                        const int jb = tj[i], tb = tt[i];
+                        float mf = od_P[i];
 #pragma unroll
                         for (int bb = 1; bb < NBT - 1; ++bb) mf *= (bb > jb && bb < tb) ? tot[bb] : 1.f;
-                        const f32x4 R = *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * jb + 4 * qd) * mf;
+                        const f32x4 R = od_S[i] * mf;
                         const unsigned ao = aoff(lA, jb, tb);
                         if (tq[i]) sts4<ET>(smem, rbm + ao, cvt4<ET>(R * acc[2 + i] * scale));
-                        else sts4<ET>(smem, L::oAn + ao, cvt4<ET>(R * acc[2 + i] * (-gv[kVb * C + t])));
+                        else sts4<ET>(smem, L::oAn + ao, cvt4<ET>(R * acc[2 + i] * (-od_b[i])));
                     }
                 }
                 // ---- T_pp = (I + A_pp)^-1 by f32 forward substitution: four
