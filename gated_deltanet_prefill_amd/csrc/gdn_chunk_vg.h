@@ -54,7 +54,8 @@ struct VgCfg : ChunkCfg<ET, DK_, DVS_, C_, NB_> {
     static constexpr int oQg = oKg + C_ * Base::LDK * Base::ES;   // Q diag(G)
     static constexpr int oKr = oQg + C_ * Base::LDK * Base::ES;   // K diag(G_last / G)
     static constexpr int oPart = oKr + C_ * Base::LDK * Base::ES;  // per-wave partial tiles
-    static constexpr int VBYTES = oPart + Base::NW * 2 * 64 * 16;
+    static constexpr int oPartX = oPart + Base::NW * 2 * 64 * 16;  // partials of the cross-block tile
+    static constexpr int VBYTES = oPartX + Base::NW * 2 * 64 * 16;
     // the diagonal tiles of one block are summed over NPART waves, each
     // taking an equal share of the key steps
     static constexpr int NPART_ = Base::NW / Base::NBT;
@@ -272,8 +273,12 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             if (L::GUNITS % NT == 0 || it < L::GUNITS) {
                 const int t = it / (DK / 4), u = it - t * (DK / 4);
                 f32x4 gv = __builtin_bit_cast(f32x4, rg[i]);
+                if (flags & kLogGate) {            // uniform: exp only for log-space gates
 #pragma unroll
-                for (int e = 0; e < 4; ++e) gv[e] = (t < cn) ? decay_of(gv[e], flags) : 1.f;
+                    for (int e = 0; e < 4; ++e) gv[e] = expf(gv[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[e] = (t < cn) ? gv[e] : 1.f;
                 *reinterpret_cast<f32x4 *>(sGv + t * LDG + 4 * u) = gv;
             }
         }
@@ -373,12 +378,16 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
             *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
         }
+        // tokens j in block 0, t in block 1: R = P16_t S16_j; every wave
+        // takes a share of the key steps and leaves its partial tile in LDS
+        constexpr int NPX = NW < NSK ? NW : NSK;         // waves sharing the cross-block tile
+        constexpr int SPX = NSK / NPX;
         if constexpr (NBT == 2) {
-            // tokens j in block 0, t in block 1: R = P16_t S16_j
-            if (wave == NW - 1) {
+            if (wave < NPX) {
                 f32x4 zk = zero4(), zq = zero4();
 #pragma unroll
-                for (int s = 0; s < NSK; ++s) {
+                for (int ss = 0; ss < SPX; ++ss) {
+                    const int s = wave * SPX + ss;
                     f32x4 ja[BLK], tk[BLK], tq[BLK];
 #pragma unroll
                     for (int h = 0; h < BLK; ++h) {
@@ -393,10 +402,9 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     zk = mfma_step(fa, frag_of<ET>(tk), zk);
                     zq = mfma_step(fa, frag_of<ET>(tq), zq);
                 }
-                const int t = 16 + x;
-                const float bv = sb[t];
-                st4<ET>(sAn + t * LDC + 4 * qd, cvt4<ET>(zk * (-bv)));
-                st4<ET>(sQKR + t * LDC + 4 * qd, cvt4<ET>(zq * scale));
+                f32x4 *px = reinterpret_cast<f32x4 *>(smem + L::oPartX) + (wave * 2) * 64 + lane;
+                px[0] = zk;
+                px[64] = zq;
             }
         }
         // K diag(G), Q diag(G), K diag(G_last / G) and G_last, elementwise
@@ -423,6 +431,22 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         }
         lds_barrier();
 
+        // ---- (c) the cross-block tile of -A and QKR from its partials (last wave)
+        if constexpr (NBT == 2) {
+            if (wave == NW - 1) {
+                f32x4 zk = zero4(), zq = zero4();
+#pragma unroll
+                for (int pp = 0; pp < NPX; ++pp) {
+                    const f32x4 *px = reinterpret_cast<const f32x4 *>(smem + L::oPartX) + (pp * 2) * 64 + lane;
+                    zk += px[0];
+                    zq += px[64];
+                }
+                const int t = 16 + x;
+                const float bv = sb[t];
+                st4<ET>(sAn + t * LDC + 4 * qd, cvt4<ET>(zk * (-bv)));
+                st4<ET>(sQKR + t * LDC + 4 * qd, cvt4<ET>(zq * scale));
+            }
+        }
         // ---- (c) diagonal inverses (waves < NBT)
         if (wave < NBT) {
             const int base = 16 * wave;

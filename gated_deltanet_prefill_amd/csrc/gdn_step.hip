@@ -56,9 +56,12 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     if constexpr (VG) {             // decay each key column first: s <- s diag(g)
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-            const f32x4 gv = *reinterpret_cast<const f32x4 *>(g + (size_t)slot * DK + 4 * (m * LPR + sub));
+            f32x4 gv = *reinterpret_cast<const f32x4 *>(g + (size_t)slot * DK + 4 * (m * LPR + sub));
+            if (flags & kLogGate) {            // uniform: exp only for log-space gates
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[m][i] *= decay_of(gv[i], flags);
+                for (int i = 0; i < 4; ++i) gv[i] = expf(gv[i]);
+            }
+            s[m] *= gv;
         }
     }
     float a = 0.f, bq = 0.f, kq = 0.f;
@@ -232,17 +235,21 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
             for (int m = 0; m < NP; ++m) gvt[m] = gvn[m];
         }
-        const float gt = VG ? 1.f : decay_of(gn, flags), bt = bn;
+        float gt = VG ? 1.f : gn;
+        if (!VG && (flags & kLogGate)) gt = expf(gt);   // uniform
+        const float bt = bn;
         if (t + 1 < T) load(t + 1);
         if constexpr (VG) {
+            if (flags & kLogGate) {            // uniform: exp only for log-space gates
 #pragma unroll
-            for (int m = 0; m < NP; ++m) {
-                f32x4 dm;
+                for (int m = 0; m < NP; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dm[i] = decay_of(gvt[m][i], flags);
-#pragma unroll
-                for (int r = 0; r < R; ++r) s[r][m] *= dm;
+                    for (int i = 0; i < 4; ++i) gvt[m][i] = expf(gvt[m][i]);
             }
+#pragma unroll
+            for (int m = 0; m < NP; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r) s[r][m] *= gvt[m];
         } else {
             c *= gt;
             if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the slot
