@@ -332,6 +332,13 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     *reinterpret_cast<f32x4 *>(sP16 + t * LDG + i0) = p16;
                     *reinterpret_cast<f32x4 *>(sS16 + t * LDG + i0) = s16;
                     if (x == 15) *reinterpret_cast<f32x4 *>(sBT + bt * DK + i0) = p16;
+                    // the scaled K and Q that need no other block: G = P16 in
+                    // the first block, G_last / G = S16 in the last
+                    if (bt == 0) {
+                        st4<ET>(sKg + t * LDK + i0, cvt4<ET>(kf * p16));
+                        st4<ET>(sQg + t * LDK + i0, cvt4<ET>(qf * p16));
+                    }
+                    if (bt == NBT - 1) st4<ET>(sKr + t * LDK + i0, cvt4<ET>(kf * s16));
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -407,27 +414,30 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 px[64] = zq;
             }
         }
-        // K diag(G), Q diag(G), K diag(G_last / G) and G_last, elementwise
+        // the scaled K and Q that need the other block's totals: K diag(G)
+        // and Q diag(G) of the second block (G = P16 x totals of the first),
+        // K diag(G_last / G) of the first (S16 x totals of the second); and
+        // G_last, elementwise
+        if constexpr (NBT == 2) {
+            constexpr int HU = 16 * DK / 4;                 // 16-byte units of one block
 #pragma unroll
-        for (int ii = 0; ii < L::PERG; ++ii) {
-            const int it = tid + ii * NT;
-            if (L::GUNITS % NT != 0 && it >= L::GUNITS) break;
-            const int t = it / (DK / 4), i0 = 4 * (it - t * (DK / 4));
-            const int blk = t >> 4;
-            f32x4 G = *reinterpret_cast<const f32x4 *>(sP16 + t * LDG + i0);
-            f32x4 Rl = *reinterpret_cast<const f32x4 *>(sS16 + t * LDG + i0);
-            if (NBT == 2 && blk == 1) G *= *reinterpret_cast<const f32x4 *>(sBT + i0);
-            if (NBT == 2 && blk == 0) Rl *= *reinterpret_cast<const f32x4 *>(sBT + DK + i0);
-            const f32x4 kf = to_f32x4<ET>(ld4<ET>(sK + t * LDK + i0));
-            const f32x4 qf = to_f32x4<ET>(ld4<ET>(sQ + t * LDK + i0));
-            st4<ET>(sKg + t * LDK + i0, cvt4<ET>(kf * G));
-            st4<ET>(sQg + t * LDK + i0, cvt4<ET>(qf * G));
-            st4<ET>(sKr + t * LDK + i0, cvt4<ET>(kf * Rl));
-            if (t == 0) {
-                f32x4 gl = *reinterpret_cast<const f32x4 *>(sBT + i0);
-                if (NBT == 2) gl *= *reinterpret_cast<const f32x4 *>(sBT + DK + i0);
-                *reinterpret_cast<f32x4 *>(sGl + i0) = gl;
+            for (int ii = 0; ii < (HU + NT - 1) / NT; ++ii) {
+                const int it = tid + ii * NT;
+                if (HU % NT != 0 && it >= HU) break;
+                const int r = it / (DK / 4), i0 = 4 * (it - r * (DK / 4));
+                const f32x4 bt0 = *reinterpret_cast<const f32x4 *>(sBT + i0);
+                const f32x4 bt1 = *reinterpret_cast<const f32x4 *>(sBT + DK + i0);
+                const int t1 = 16 + r;
+                const f32x4 G = *reinterpret_cast<const f32x4 *>(sP16 + t1 * LDG + i0) * bt0;
+                st4<ET>(sKg + t1 * LDK + i0, cvt4<ET>(to_f32x4<ET>(ld4<ET>(sK + t1 * LDK + i0)) * G));
+                st4<ET>(sQg + t1 * LDK + i0, cvt4<ET>(to_f32x4<ET>(ld4<ET>(sQ + t1 * LDK + i0)) * G));
+                const f32x4 Rl = *reinterpret_cast<const f32x4 *>(sS16 + r * LDG + i0) * bt1;
+                st4<ET>(sKr + r * LDK + i0, cvt4<ET>(to_f32x4<ET>(ld4<ET>(sK + r * LDK + i0)) * Rl));
+                if (r == 0) *reinterpret_cast<f32x4 *>(sGl + i0) = bt0 * bt1;
             }
+        } else {
+            for (int i0 = 4 * tid; i0 < DK; i0 += 4 * NT)
+                *reinterpret_cast<f32x4 *>(sGl + i0) = *reinterpret_cast<const f32x4 *>(sBT + i0);
         }
         lds_barrier();
 
