@@ -7,6 +7,43 @@
 
 namespace gdn {
 
+// Generic kernel on value slices of DVS columns: Dv / DVS workgroups per
+// slot, each recomputing the slot's C x C work (gate products, K K^T, the
+// solve) for its own slice of the state.
+template <typename ET, int DK, int DV, int C, int DVS>
+hipError_t launch_generic(const FwdArgs &a, hipStream_t st) {
+    // 32 value columns per wave for a 128-column slice, else 16 (more waves,
+    // fewer live registers per wave at small slices)
+    constexpr int NB = DVS >= 128 ? 2 : 1;
+    using L = ChunkCfg<ET, DK, DVS, C, NB>;
+    const long nslots = (long)a.B * a.Hv;
+    const int group = a.Hv / a.Hk;
+    const int nsplit = DV / DVS;
+    const long nblocks = nslots * nsplit;
+    const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
+    hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), dim3((unsigned)nblocks), dim3(L::NT), 0, st,
+                       static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
+                       static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale,
+                       a.flags);
+    return hipGetLastError();
+}
+
+// Value slices per slot for the generic kernel, from timed sweeps over slot
+// counts 8..384, T = 128 and 512, Dk = Dv in {64, 128}: while B Hv is small
+// the extra workgroups fill idle CUs (up to 1.4x faster), once the grid
+// fills the duplicated C x C work costs more than it gains.
+inline int generic_split(int Dv, int C, bool f32, long nslots) {
+    if (Dv == 128) {
+        if (f32) return (C == 16 && nslots <= 128) ? 2 : 1;
+        if (C == 32) return nslots <= 24 ? 4 : nslots <= 384 ? 2 : 1;
+        if (C == 16) return nslots <= 16 ? 4 : nslots <= 128 ? 2 : 1;
+        return 1;
+    }
+    if (Dv == 64 && !f32 && C == 16) return nslots <= 64 ? 2 : 1;
+    return 1;
+}
+
 template <typename ET, int DK, int DV, int C>
 hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
     const long nslots = (long)a.B * a.Hv;
@@ -20,21 +57,16 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
                            static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale, a.flags);
         return hipGetLastError();
     } else {
-        // 32 value columns per wave for Dv = 128, else 16 (more waves, fewer
-        // live registers per wave at small Dv)
-        constexpr int NB = DV >= 128 ? 2 : 1;
-        constexpr int DVS = DV;                      // one workgroup per slot
-        using L = ChunkCfg<ET, DK, DVS, C, NB>;
-        const int nsplit = DV / DVS;
-        const long nblocks = nslots * nsplit;
-        const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
-        const dim3 grid((unsigned)nblocks), block(L::NT);
-        hipLaunchKernelGGL((chunk_fwd_kernel<ET, DK, DVS, C, NB>), grid, block, 0, st,
-                           static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
-                           static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale,
-                           a.flags);
-        return hipGetLastError();
+        constexpr bool F32 = sizeof(ET) == 4;
+        const int split = generic_split(DV, C, F32, nslots);
+        if constexpr (DV == 128 && (C == 16 || (!F32 && C == 32))) {
+            if constexpr (!F32)
+                if (split == 4) return launch_generic<ET, DK, DV, C, 32>(a, st);
+            if (split == 2) return launch_generic<ET, DK, DV, C, 64>(a, st);
+        } else if constexpr (DV == 64 && !F32 && C == 16) {
+            if (split == 2) return launch_generic<ET, DK, DV, C, 32>(a, st);
+        }
+        return launch_generic<ET, DK, DV, C, DV>(a, st);
     }
 }
 
