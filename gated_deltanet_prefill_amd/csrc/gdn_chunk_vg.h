@@ -137,7 +137,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                      const ET *__restrict__ v, const float *__restrict__ g,
                      const float *__restrict__ beta, const float *state_in,
                      float *state_out, ET *__restrict__ y,
-                     int T, int Hk, int Hv, int Dv, int xcd_group, float scale, int flags)
+                     int T, int Hk, int Hv, int Dv, int nsplit, int xcd_group, float scale, int flags)
 {
     using L = VgCfg<ET, DK, DVS, C, NB>;
     using X4 = typename Vec<ET>::x4;
@@ -178,16 +178,18 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int sib = kk % xcd_group, m = kk / xcd_group;
         bid = (m * 8 + xcd) * xcd_group + sib;
     }
-    const int b = bid / Hv, hv = value_head_of_rank(bid % Hv, Hk, Hv, flags);
+    // workgroup = (slot rank, value slice vs of DVS columns)
+    const int rank = bid / nsplit, vs = bid - rank * nsplit;
+    const int b = rank / Hv, hv = value_head_of_rank(rank % Hv, Hk, Hv, flags);
     const int hk = key_head(hv, Hk, Hv, flags);
     const int slot = b * Hv + hv;
-    const int vloc = wave * 16 * NB;
+    const int vloc = wave * 16 * NB;               // first slice column of this wave
 
     f32x4 S[NBK][NB];
     const size_t sbase = (size_t)slot * Dv * DK;
 #pragma unroll
     for (int vb = 0; vb < NB; ++vb) {
-        const size_t row = sbase + (size_t)(vloc + 16 * vb + x) * DK;
+        const size_t row = sbase + (size_t)(vs * DVS + vloc + 16 * vb + x) * DK;
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
             S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + 16 * kb + 4 * qd)
@@ -205,7 +207,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * Dv, gstride = (size_t)Hv * DK;
     const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
     const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
-    const ET *vbase = v + ((size_t)b * T * Hv + hv) * Dv;
+    const ET *vbase = v + ((size_t)b * T * Hv + hv) * Dv + vs * DVS;
     const float *gbase = g + ((size_t)b * T * Hv + hv) * DK;
     const float *bbase = beta + (size_t)b * T * Hv + hv;
 
@@ -566,7 +568,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
         }
-        store_y(y + (((size_t)b * T + t0) * Hv + hv) * Dv, Hv * Dv, cn, vloc, x, qd, Ya);
+        store_y(y + (((size_t)b * T + t0) * Hv + hv) * Dv + vs * DVS, Hv * Dv, cn, vloc, x, qd, Ya);
 
         // ---- (f) S^T <- diag(G_last) S^T + (K diag(G_last / G))^T D
 #pragma unroll
@@ -595,27 +597,39 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 
 #pragma unroll
     for (int vb = 0; vb < NB; ++vb) {
-        const size_t row = sbase + (size_t)(vloc + 16 * vb + x) * DK;
+        const size_t row = sbase + (size_t)(vs * DVS + vloc + 16 * vb + x) * DK;
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
             *reinterpret_cast<f32x4 *>(state_out + row + 16 * kb + 4 * qd) = S[kb][vb];
     }
 }
 
+// Value slices per slot while B Hv is small: every slice repeats the chunk's
+// scans and C x C work for its own columns of the state.
+// Value slices per slot: two slices of 64 columns for Dv = 128 while B Hv
+// <= 128, each repeating the chunk's scans and C x C work for its half of
+// the state (timed sweep over B Hv = 8..384, T = 128 and 512: 1.1-1.2x for
+// 16-bit inputs, 1.3x for float32; slices of 32 columns leave two waves per
+// workgroup and are slower, as is any split for Dv = 64).
+inline int vg_split(int Dv, long nslots) { return (Dv == 128 && nslots <= 128) ? 2 : 1; }
+
+// One slice of DVS value columns per workgroup, Dv / DVS workgroups per slot.
 // Chunk length: 32 for 16-bit inputs, 16 for float32 (LDS budget).
-template <typename ET, int DK, int DV>
-hipError_t launch_chunk_vg_dv(const FwdArgs &a, hipStream_t st) {
-    constexpr int NB = DV >= 128 ? 2 : 1;
+template <typename ET, int DK, int DV, int DVS>
+hipError_t launch_chunk_vg_slices(const FwdArgs &a, hipStream_t st) {
+    constexpr int NB = DVS >= 128 ? 2 : 1;
     const long nslots = (long)a.B * a.Hv;
     const int group = a.Hv / a.Hk;
-    const int xcd_group = (group > 1 && nslots % (8L * group) == 0) ? group : 1;
+    const int nsplit = DV / DVS;
+    const long nblocks = nslots * nsplit;
+    const int xcd_group = (nsplit == 1 && group > 1 && nblocks % (8L * group) == 0) ? group : 1;
     auto go = [&](auto cc) -> hipError_t {
         constexpr int C = decltype(cc)::value;
-        using L = VgCfg<ET, DK, DV, C, NB>;
-        hipLaunchKernelGGL((chunk_vg_kernel<ET, DK, DV, C, NB>), dim3((unsigned)nslots), dim3(L::NT), 0, st,
+        using L = VgCfg<ET, DK, DVS, C, NB>;
+        hipLaunchKernelGGL((chunk_vg_kernel<ET, DK, DVS, C, NB>), dim3((unsigned)nblocks), dim3(L::NT), 0, st,
                            static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                            static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, xcd_group, a.scale, a.flags);
+                           static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, nsplit, xcd_group, a.scale, a.flags);
         return hipGetLastError();
     };
     if constexpr (sizeof(ET) == 4) {
@@ -624,6 +638,13 @@ hipError_t launch_chunk_vg_dv(const FwdArgs &a, hipStream_t st) {
         if (a.C == 16) return go(std::integral_constant<int, 16>{});
         return go(std::integral_constant<int, 32>{});
     }
+}
+
+template <typename ET, int DK, int DV>
+hipError_t launch_chunk_vg_dv(const FwdArgs &a, hipStream_t st) {
+    if constexpr (DV == 128)
+        if (vg_split(DV, (long)a.B * a.Hv) == 2) return launch_chunk_vg_slices<ET, DK, DV, 64>(a, st);
+    return launch_chunk_vg_slices<ET, DK, DV, DV>(a, st);
 }
 
 template <typename ET, int DK>

@@ -3,7 +3,7 @@ against the f64 oracle: the chunked kernel for vector gates at C = 16 and
 32 (16 for float32), the sequential kernel and the decode step; every dtype
 and head size, grouped and tiled heads, log gates, ragged lengths, gate
 extremes (zero, tiny and unit decays per column), in-place state and the
-automatic kernel choice.
+automatic kernel choice, and Dv = 128 on both sides of the value-slice threshold.
 """
 import numpy as np
 import pytest
@@ -136,3 +136,21 @@ def test_vector_gate_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for y, s in outs[1:]:
         assert torch.equal(y, outs[0][0]) and torch.equal(s, outs[0][1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hk,Hv", [(4, 16, 32), (3, 43, 43)], ids=["128slots", "129slots"])
+def test_vector_gate_value_slices(gpu_lib, dtype, B, Hk, Hv):
+    """Dv = 128 runs two 64-column value slices per slot up to B Hv = 128
+    slots and one workgroup per slot above: both sides of the threshold, on
+    sampled slots."""
+    inp = vg_inputs(B, 45, Hk, Hv, 128, 128, dtype, seed=B * Hv)
+    y, s = run(gpu_lib, inp, 16 if dtype == "f32" else 32)
+    rng = np.random.default_rng(B * Hv)
+    mask = np.zeros((B, Hv), bool)
+    mask.reshape(-1)[rng.choice(B * Hv, 12, replace=False)] = True
+    mask[-1, -1] = True
+    yr, sr = oracle_run(inp, slot_mask=mask)
+    assert_parity(y, s, yr, sr, dtype, f"vector gate {B * Hv} slots {dtype}",
+                  np.broadcast_to(mask[:, None, :, None], yr.shape),
+                  np.broadcast_to(mask[:, :, None, None], sr.shape))
