@@ -604,8 +604,6 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     }
 }
 
-// Value slices per slot while B Hv is small: every slice repeats the chunk's
-// scans and C x C work for its own columns of the state.
 // Value slices per slot: two slices of 64 columns for Dv = 128 while B Hv
 // <= 128, each repeating the chunk's scans and C x C work for its half of
 // the state (timed sweep over B Hv = 8..384, T = 128 and 512: 1.1-1.2x for
