@@ -60,6 +60,7 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s + TFLOP/s (chunk) and state GB/s (step), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, TFLOP/s
+F32_PEAK_TFLOPS = 157.3          # MI355X dense fp32 MFMA, TFLOP/s
 PREFILL = dict(B=8, T=8192, Hk=16, Hv=32, Dk=128, Dv=128, C=64, dtype="bf16")
 DECODE = dict(B=64, T=256, Hk=16, Hv=32, Dk=128, Dv=128, dtype="f16")
 CHUNK_KERNEL_SOURCES = ["gdn_chunk_pipe.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_internal.h",
@@ -187,6 +188,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--no-vector-gate", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args()
@@ -435,6 +437,50 @@ def main():
             "method": "state ping-pongs between two buffers; 512 MiB scratch read between "
                       "calls; each call timed alone with HIP events; 16 calls per entry",
             "hbm_bytes": "state read + write once per call plus q, k, v, y, g, beta of T tokens",
+        }
+
+    # ---------------- the other prefill workloads (parity-test cases): times only
+    if not args.no_configs:
+        rows = []
+        for name in ("tiny_f32", "bonsai_prefill", "gqa_ragged"):
+            W = gi.WORKLOADS[name]
+            winp = gi.workload_inputs(name)
+            dt = W["dtype"]
+            wq, wk, wv = (upload(winp[n], dt) for n in ("q", "k", "v"))
+            wg, wb = upload(winp["g"], "f32"), upload(winp["beta"], "f32")
+            ws = upload(winp["state"], "f32") if winp["state"] is not None else None
+            wso = torch.empty((W["B"], W["Hv"], W["Dv"], W["Dk"]), dtype=torch.float32, device=dev)
+            wy = torch.empty_like(wv)
+            es = 4 if dt == "f32" else 2
+            row = {"workload": name, "B": W["B"], "T": W["T"], "Hk": W["Hk"], "Hv": W["Hv"],
+                   "Dk": W["Dk"], "Dv": W["Dv"], "dtype": dt}
+            for label, C in (("named_C", W["C"]), ("auto", 0)):
+                call = lambda: gdn.chunk_fwd(wq, wk, wv, wg, wb, ws, C=C, state_out=wso, y=wy, stream=stream)
+                for _ in range(20):
+                    call()
+                torch.cuda.synchronize()
+                n = 50
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                row[f"{label}_us"] = e0.elapsed_time(e1) * 1e3 / n
+            row["C"] = W["C"]
+            sec = row["named_C_us"] * 1e-6
+            nb = prefill_bytes(**W, es=es)
+            nf = prefill_flops(**W)
+            row["tokens_per_s"] = W["B"] * W["T"] / sec
+            row["hbm_frac"] = nb / sec / 1e9 / HBM_PEAK_GBS
+            row["mfma_frac"] = nf / sec / 1e12 / (F32_PEAK_TFLOPS if dt == "f32" else BF16_PEAK_TFLOPS)
+            rows.append(row)
+            del wq, wk, wv, wg, wb, ws, wso, wy
+        out["configs"] = {
+            "rows": rows,
+            "method": "50 back-to-back launches after 20 warm-up launches, HIP events; at the "
+                      "workload's named C and with the automatic choice (C = 0); fractions at "
+                      "the named C against HBM and against the MFMA peak of the input dtype",
         }
 
     # ---------------- CPU oracle on a bounded sample
