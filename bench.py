@@ -455,18 +455,31 @@ def main():
             row = {"workload": name, "B": W["B"], "T": W["T"], "Hk": W["Hk"], "Hv": W["Hv"],
                    "Dk": W["Dk"], "Dv": W["Dv"], "dtype": dt}
             for label, C in (("named_C", W["C"]), ("auto", 0)):
-                call = lambda: gdn.chunk_fwd(wq, wk, wv, wg, wb, ws, C=C, state_out=wso, y=wy, stream=stream)
-                for _ in range(20):
-                    call()
+                # 50 launches captured in one HIP graph and replayed, so that the
+                # time is the GPU's and not the host's per-call overhead
+                call = lambda: gdn.chunk_fwd(wq, wk, wv, wg, wb, ws, C=C, state_out=wso, y=wy)
+                side = torch.cuda.Stream(dev)
+                side.wait_stream(torch.cuda.current_stream(dev))
+                with torch.cuda.stream(side):
+                    for _ in range(3):
+                        call()
+                torch.cuda.current_stream(dev).wait_stream(side)
                 torch.cuda.synchronize()
                 n = 50
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for _ in range(n):
+                        call()
+                for _ in range(3):
+                    graph.replay()
+                torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                for _ in range(n):
-                    call()
+                graph.replay()
                 e1.record(stream)
                 torch.cuda.synchronize()
                 row[f"{label}_us"] = e0.elapsed_time(e1) * 1e3 / n
+                del graph
             row["C"] = W["C"]
             sec = row["named_C_us"] * 1e-6
             nb = prefill_bytes(**W, es=es)
@@ -478,8 +491,8 @@ def main():
             del wq, wk, wv, wg, wb, ws, wso, wy
         out["configs"] = {
             "rows": rows,
-            "method": "50 back-to-back launches after 20 warm-up launches, HIP events; at the "
-                      "workload's named C and with the automatic choice (C = 0); fractions at "
+            "method": "50 launches captured in a HIP graph, replayed after 3 warm-up replays, "
+                      "HIP events around one replay; at the workload's named C and with the automatic choice (C = 0); fractions at "
                       "the named C against HBM and against the MFMA peak of the input dtype",
         }
 
