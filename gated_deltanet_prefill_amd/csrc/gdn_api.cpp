@@ -82,20 +82,24 @@ int check(const void *q, const void *k, const void *v, const float *g,
 // chunked kernel runs its products at the float32 MFMA rate).
 bool seq_for(int dtype, int T) { return T <= (dtype == GDN_F32 ? 12 : 6); }
 
-// Chunk length: 16 keeps the most work in flight per token and wins on
-// grids of many (batch, head) slots; the pipelined 64-token kernel (16-bit
-// inputs, 128-dimensional heads) wins once each slot has enough chunks to
-// fill its pipeline, which takes more tokens the more slots share the chip.
-// For other 16-bit head sizes 32 wins from about 64 tokens; for float32
-// inputs 16 is never more than a few percent off.
+// Chunk length, from timed sweeps of GPU time (launches replayed from a HIP
+// graph) over B Hv = 2..1024, T = 2..1111, Dk/Dv in {32, 64, 128}, all
+// dtypes.  16 keeps the most work in flight per token and wins on grids of
+// many (batch, head) slots and on short sequences; 32 wins from 32 tokens on
+// grids of up to 256 slots (the generic kernel then runs several value
+// slices per slot); the pipelined 64-token kernel (16-bit inputs,
+// 128-dimensional heads) wins once each slot has enough chunks to fill its
+// pipeline, which takes more tokens the more slots share the chip.  float32
+// inputs run their products at the f32 MFMA rate: 16 for 128-dimensional
+// heads, 32 from 32 tokens for smaller ones.
 int chunk_for(int dtype, int Dk, int Dv, long slots, int T) {
-    if (dtype != GDN_F32 && Dk == 128 && Dv == 128) {
-        if (T >= 48 && 16L * T >= 3L * slots) return 64;
-        if (T >= 16 && slots <= 256) return 32;
-    } else if (dtype != GDN_F32 && T >= 64) {
-        return 32;
+    if (dtype == GDN_F32) return (Dk <= 64 && Dv <= 64 && T >= 32) ? 32 : 16;
+    if (Dk == 128 && Dv == 128) {
+        if (16L * T >= 3L * slots && (T >= 96 || (T >= 48 && slots > 256))) return 64;
+        if (T >= 32 && slots <= 256) return 32;
+        return 16;
     }
-    return 16;
+    return (T >= 64 || (T >= 32 && slots <= 256)) ? 32 : 16;
 }
 
 int launch(const gdn::FwdArgs &a, int dtype, bool seq, hipStream_t stream) {

@@ -149,12 +149,14 @@ def test_seq_long_sequence(gpu_lib):
     assert_parity(y, s, yr, sr, "bf16", "seq T=600")
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_auto_chunk(gpu_lib, dtype):
+def test_auto_chunk(gpu_lib, dtype, D):
     """C = 0: the library's own choice of kernel and chunk length is right
-    on both sides of the switch from token-by-token to chunked."""
-    for T in (1, 3, 8, 15, 16, 17, 40, 100, 300):
-        inp = gi.make_inputs(2, T, 2, 4, 128, 128, dtype, gate="sigmoid", state_std=0.2, seed=500 + T)
+    on both sides of every switch (token-by-token to chunked, C = 16 / 32 /
+    64)."""
+    for T in (1, 3, 8, 12, 13, 15, 16, 17, 31, 32, 40, 47, 48, 63, 64, 95, 96, 100, 300):
+        inp = gi.make_inputs(2, T, 2, 4, D, D, dtype, gate="sigmoid", state_std=0.2, seed=500 + T + D)
         d = upload(inp)
         y, s = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=0)
         torch.cuda.synchronize()
