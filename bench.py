@@ -500,7 +500,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         nthreads = len(os.sched_getaffinity(0))
-        nb = 4                                   # 4 of the 8 batch elements
+        nb = P["B"]                              # the whole long prefill
         qs, ks, vs = (gi.decode(inp[n][:nb], "bf16") for n in ("q", "k", "v"))
         gs, bs = inp["g"][:nb].astype(np.float64), inp["beta"][:nb].astype(np.float64)
         ss = inp["state"][:nb].astype(np.float64)
@@ -509,9 +509,9 @@ def main():
         cpu_s = time.perf_counter() - t0
         out["cpu_baseline"] = {
             "value": nb * P["T"] / cpu_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{nb} of the {P['B']} batch elements of the long prefill: {nb} x {P['T']} "
-                      f"tokens x {P['Hv']} value heads (float64 sequential rule, OpenMP over "
-                      f"(batch, head) slots), {cpu_s:.2f} s",
+            "sample": f"the whole long prefill, {nb} x {P['T']} tokens x {P['Hv']} value heads "
+                      f"(float64 sequential rule, OpenMP over (batch, head) slots), {cpu_s:.2f} s "
+                      f"on {nthreads} threads",
         }
     print(json.dumps(out), flush=True)
 
