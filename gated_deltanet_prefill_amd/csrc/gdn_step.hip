@@ -22,6 +22,29 @@ constexpr int kStepLanesPerRow = 8;
 // four value rows per lane
 constexpr long kSeqMinWaves = 2048;
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// sum over the eight lanes of an aligned group (every lane gets the sum):
+// swap neighbours, swap pairs, then add the mirror lane of the half row
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp_mov<0xb1>(x);      // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4e>(x);      // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);     // row_half_mirror
+    return x;
+}
+
+// A row of zeros read in place of state_in when it is NULL, so that the state
+// loads are unconditional (a branch around each load made the compiler wait
+// for every load before issuing the next).
+static __device__ const float kZeroRow[128] = {};
+// global-memory pointers (address space 1), so that the loads stay global
+// loads after the select between state_in and kZeroRow
+typedef const float __attribute__((address_space(1))) gfloat;
+typedef const f32x4 __attribute__((address_space(1))) gf32x4;
+
 // VG: g is [B,Hv,Dk], one decay per key dimension (column i of the state
 // decays by g_i); else one decay per (batch, value head).
 template <typename ET, int DK, bool VG>
@@ -44,6 +67,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const ET *kp = k + ((size_t)b * Hk + hk) * DK;
     const ET *qp = q + ((size_t)b * Hk + hk) * DK;
     const size_t row = ((size_t)slot * Dv + j) * DK;
+    gfloat *sin = state_in ? (gfloat *)state_in + row : (gfloat *)kZeroRow;
 
     f32x4 s[NP], kv[NP], qv[NP];
 #pragma unroll
@@ -51,7 +75,7 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int e = 4 * (m * LPR + sub);
         kv[m] = to_f32x4<ET>(ld4<ET>(kp + e));
         qv[m] = to_f32x4<ET>(ld4<ET>(qp + e));
-        s[m] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + e) : zero4();
+        s[m] = *reinterpret_cast<gf32x4 *>(sin + e);
     }
     if constexpr (VG) {             // decay each key column first: s <- s diag(g)
 #pragma unroll
@@ -74,12 +98,10 @@ void step_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             kq += kv[m][i] * qv[m][i];
         }
     }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) {
-        a += __shfl_xor(a, off);
-        bq += __shfl_xor(bq, off);
-        kq += __shfl_xor(kq, off);
-    }
+    static_assert(LPR == 8, "sum8 reduces over aligned groups of eight lanes");
+    a = sum8(a);
+    bq = sum8(bq);
+    kq = sum8(kq);
     const float gt = VG ? 1.f : decay_of(g[slot], flags), bt = beta[slot];
     const float vj = to_f32(v[(size_t)slot * Dv + j]);
     const float d = bt * (vj - gt * a);
@@ -135,20 +157,6 @@ static hipError_t launch_step_typed(const FwdArgs &a, hipStream_t st) {
 //     S' <- S' + (d / c) k,  y = (b + d (k . q)) / sqrt(Dk)
 // which is the step's arithmetic with g S applied lazily.  The next token's
 // k, q, v, g and beta are loaded while the current one runs.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-// sum over the eight lanes of an aligned group (every lane gets the sum):
-// swap neighbours, swap pairs, then add the mirror lane of the half row
-__device__ __forceinline__ float sum8(float x) {
-    x += dpp_mov<0xb1>(x);      // quad_perm [1,0,3,2]
-    x += dpp_mov<0x4e>(x);      // quad_perm [2,3,0,1]
-    x += dpp_mov<0x141>(x);     // row_half_mirror
-    return x;
-}
-
 template <typename ET, int R> struct RowVec;
 template <typename ET> struct RowVec<ET, 1> {
     using T = ET;
@@ -193,13 +201,15 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     ET *yp = y + ((size_t)b * T * Hv + hv) * Dv + j0;
     const size_t row0 = ((size_t)slot * Dv + j0) * DK + 4 * sub;
 
+    // rows of zeros (stride 0) when there is no initial state
+    gfloat *sin = state_in ? (gfloat *)state_in + row0 : (gfloat *)kZeroRow + 4 * sub;
+    const int sstride = state_in ? DK : 0;
     f32x4 s[R][NP];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < NP; ++m)
-            s[r][m] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row0 + (size_t)r * DK + 32 * m)
-                               : zero4();
+            s[r][m] = *reinterpret_cast<gf32x4 *>(sin + (size_t)r * sstride + 32 * m);
     typename Vec<ET>::x4 kn[NP], qn[NP];
     typename RV::T vn{};
     float gn = 0.f, bn = 0.f;
