@@ -1,7 +1,8 @@
 """GPU parity at sizes whose element offsets pass 2^31 (64-bit indexing):
 the long-prefill shape at B = 64 (y and v hold 2^31 elements, 4 GiB each in
 bf16) through the pipelined chunk kernel, and the decode shapes at B = 4096
-through the sequential kernel and the step (an 8 GiB state).  Inputs are
+through the sequential kernel and the step (an 8 GiB state); and the long
+prefill with a decay per key dimension at its full size.  Inputs are
 drawn on the device from a seeded generator; the oracle checks the last
 (batch, head) slots, whose offsets are the largest, and one early slot.
 """
@@ -67,4 +68,21 @@ def test_decode_b4096(gpu_lib):
     check_slots(q, k, v, g, beta, s0, y, s, slots, "f16")
     check_slots(q, k, v, g, beta, s0, torch.stack(ys, 1), st, slots, "f16")
     del q, k, v, g, beta, s0, y, s, st, ys
+    torch.cuda.empty_cache()
+
+
+def test_vector_gate_long_prefill(gpu_lib):
+    """The long prefill with a decay per key dimension in the launch
+    configuration the bench times (C = 32, one workgroup per slot), checked
+    on sampled slots over all 8192 tokens."""
+    B, T, Hk, Hv, D = 8, 8192, 16, 32, 128
+    q, k, v, g, beta, s0 = device_inputs(B, T, Hk, Hv, D, torch.bfloat16, seed=13)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(14)
+    gvec = 0.95 + 0.05 * torch.rand((B, T, Hv, D), generator=gen, device="cuda")
+    y, s = gpu_lib.chunk_fwd(q, k, v, gvec, beta, s0, C=32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(s).all()
+    check_slots(q, k, v, gvec, beta, s0, y, s, [(7, 31), (3, 16), (0, 1)], "bf16")
+    del q, k, v, g, gvec, beta, s0, y, s
     torch.cuda.empty_cache()
