@@ -262,21 +262,18 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // ---- the state, S^T tiles [key block][value block], f32 accumulators
     f32x4 S[NBK][NB];
     const size_t sbase = (size_t)slot * Dv * DK;
+    {
+        // rows of zeros (stride 0) when there is no initial state
+        gfloat *sin = state_in ? (gfloat *)state_in + sbase : (gfloat *)kZeroRow;
+        const size_t rstride = state_in ? DK : 0;
 #pragma unroll
-    for (int vb = 0; vb < NB; ++vb) {
-        const size_t row = sbase + (size_t)(vs * DVS + vloc + 16 * vb + x) * DK;
+        for (int vb = 0; vb < NB; ++vb) {
+            const size_t row = (size_t)(vs * DVS + vloc + 16 * vb + x) * rstride;
 #pragma unroll
-        for (int kb = 0; kb < NBK; ++kb)
-            S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + 16 * kb + 4 * qd)
-                                 : zero4();
+            for (int kb = 0; kb < NBK; ++kb)
+                S[kb][vb] = *reinterpret_cast<gf32x4 *>(sin + row + 16 * kb + 4 * qd);
+        }
     }
-    // Consume the loaded state here, before the chunk loop, so that no load
-    // is still pending at the loop header (where a wait would otherwise be
-    // placed on every iteration).
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
 
     // ---- -A and QKR above the diagonal blocks stay zero; clear them once
     for (int i = tid; i < (L::oAd - L::oAn) / 16; i += NT)
@@ -395,10 +392,16 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // chunk 0 is staged before the loop; inside, chunk n+1 is loaded into
     // registers at the top of iteration n and staged into LDS at its bottom,
     // once chunk n is done with LDS.
-    if (nchunks > 0) {
-        prefetch(0);
-        stage(min(C, T));
-    }
+    // chunk 0's loads are issued while the state is still in flight; then
+    // the loaded state is consumed here, before the chunk loop, so that no
+    // load is still pending at the loop header (where a wait would otherwise
+    // be placed on every iteration)
+    if (nchunks > 0) prefetch(0);
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+    if (nchunks > 0) stage(min(C, T));
 
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;

@@ -383,12 +383,16 @@ void chunk_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             issue_q(0);
         }
         if (nchunks > 1) load_gb(1);                 // awaited before the first barrier
+        {
+            // rows of zeros (stride 0) when there is no initial state
+            gfloat *sin = state_in ? (gfloat *)state_in + sbase : (gfloat *)kZeroRow;
+            const size_t rstride = state_in ? DK : 0;
 #pragma unroll
-        for (int vb = 0; vb < NB; ++vb)
+            for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
-            for (int kb = 0; kb < NBK; ++kb)
-                S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd))
-                                     : zero4();
+                for (int kb = 0; kb < NBK; ++kb)
+                    S[kb][vb] = *reinterpret_cast<gf32x4 *>(sin + (size_t)vcol(vb, x) * rstride + kcol(kb, qd));
+        }
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll

@@ -189,16 +189,13 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const size_t sbase = (size_t)slot * Dv * DK;
 #pragma unroll
     for (int vb = 0; vb < NB; ++vb) {
-        const size_t row = sbase + (size_t)(vs * DVS + vloc + 16 * vb + x) * DK;
+        // rows of zeros (stride 0) when there is no initial state
+        gfloat *sin = state_in ? (gfloat *)state_in + sbase : (gfloat *)kZeroRow;
+        const size_t row = (size_t)(vs * DVS + vloc + 16 * vb + x) * (state_in ? DK : 0);
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
-            S[kb][vb] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + row + 16 * kb + 4 * qd)
-                                 : zero4();
+            S[kb][vb] = *reinterpret_cast<gf32x4 *>(sin + row + 16 * kb + 4 * qd);
     }
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
 
     // -A and QKR above the diagonal blocks stay zero
     for (int i = tid; i < (L::oAd - L::oAn) / 16; i += NT)
@@ -288,10 +285,14 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     };
 
     const int nchunks = (T + C - 1) / C;
-    if (nchunks > 0) {
-        prefetch(0);
-        stage(min(C, T));
-    }
+    // chunk 0's loads go out while the state is in flight; the state is then
+    // consumed here, so that no load is pending at the loop header
+    if (nchunks > 0) prefetch(0);
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+    if (nchunks > 0) stage(min(C, T));
 
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;

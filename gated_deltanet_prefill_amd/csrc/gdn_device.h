@@ -80,6 +80,15 @@ __device__ __forceinline__ f32x4 to_f32x4(typename Vec<T>::x4 a) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// A row of zeros read in place of state_in when it is NULL, so that the state
+// loads are unconditional (a branch around each load made the compiler wait
+// for every load before issuing the next).  Pointers into it and into
+// state_in are global-memory pointers (address space 1), so that the loads
+// stay global loads after the select.
+static __device__ const float kZeroRow[128] = {};
+typedef const float __attribute__((address_space(1))) gfloat;
+typedef const f32x4 __attribute__((address_space(1))) gf32x4;
+
 // One 16x16 MFMA step over 32 (16-bit types) or 4 (f32) contraction
 // indices: acc += A_frag * B_frag.
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {

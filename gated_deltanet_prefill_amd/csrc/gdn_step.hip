@@ -36,14 +36,6 @@ __device__ __forceinline__ float sum8(float x) {
     return x;
 }
 
-// A row of zeros read in place of state_in when it is NULL, so that the state
-// loads are unconditional (a branch around each load made the compiler wait
-// for every load before issuing the next).
-static __device__ const float kZeroRow[128] = {};
-// global-memory pointers (address space 1), so that the loads stay global
-// loads after the select between state_in and kZeroRow
-typedef const float __attribute__((address_space(1))) gfloat;
-typedef const f32x4 __attribute__((address_space(1))) gf32x4;
 
 // VG: g is [B,Hv,Dk], one decay per key dimension (column i of the state
 // decays by g_i); else one decay per (batch, value head).
