@@ -30,9 +30,11 @@ printed with:
                   sequential kernel (``gdn_seq_fwd``), the chunked kernel at
                   C = 16 and the library's own choice (C = 0), each call
                   timed alone with the state coming from HBM;
-* ``cpu_baseline`` the float64 CPU oracle timed on a bounded sample of the
-                  same workload (4 of the 8 batch elements: all heads, all
-                  8192 tokens), with the thread count it used.
+* ``cpu_baseline`` the float64 CPU oracle timed on the same workload (all
+                  8 batch elements, all heads, all 8192 tokens: about 40
+                  thread-seconds), with the thread count it used; the
+                  tiny, Bonsai-shaped and GQA ragged workloads are also
+                  timed on one thread.
 
 ``--copy-calibration N`` instead times a plain device copy of N MiB (used to
 scale the HBM byte counters); it prints its own JSON line.
@@ -158,6 +160,106 @@ def summarize_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib=102
     print(json.dumps(rec))
 
 
+STEP_KERNEL = "step_kernel"
+STEP_SOURCES = ["gdn_step.hip", "gdn_device.h", "gdn_internal.h"]
+
+
+def step_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in STEP_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_prefill_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_step_traffic(kind, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib=1024):
+    """HBM bytes per decode-step dispatch from FETCH_SIZE / WRITE_SIZE runs of
+    ``bench.py --decode-only KIND``, each counter scaled by what it reads for a
+    plain copy of known size."""
+    kib = copy_mib * 1024.0
+
+    def pick(means, needle):
+        hits = [v for k, v in means.items() if needle in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {needle!r} in counter results")
+        return max(hits)
+
+    copy_fetch = pick(_counter_means(cfetch_dir, "FETCH_SIZE"), "copyBuffer")
+    copy_write = pick(_counter_means(cwrite_dir, "WRITE_SIZE"), "copyBuffer")
+    f_scale, w_scale = kib / copy_fetch, kib / copy_write
+    fetch = pick(_counter_means(fetch_dir, "FETCH_SIZE"), STEP_KERNEL)
+    write = pick(_counter_means(write_dir, "WRITE_SIZE"), STEP_KERNEL)
+    sbytes, tbytes = step_bytes(**DECODE)
+    rec = {
+        "kernel": "step_kernel<f16>, decode (B=64, Hk=16, Hv=32, Dk=Dv=128)",
+        "kind": kind, "source_hash": step_source_hash(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "copy_calibration_mib": copy_mib, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "read_bytes_per_step": fetch * f_scale * 1024,
+        "write_bytes_per_step": write * w_scale * 1024,
+        "bytes_per_step": (fetch * f_scale + write * w_scale) * 1024,
+        "algorithmic_bytes_per_step": tbytes, "algorithmic_state_bytes_per_step": sbytes,
+    }
+    path = os.path.join(ROOT, "profiles", f"step_decode_{kind}_hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def decode_only(kind: str, nsteps: int):
+    """The decode loop alone: 256 chained steps with the state in place, or
+    with the state ping-ponged between two buffers and a 512 MiB scratch
+    buffer read between steps (every step then reads its state from HBM)."""
+    import numpy as np
+    import torch
+
+    import gated_deltanet_prefill_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.load()
+    dev = torch.device("cuda", 0)
+    D = DECODE
+    dinp = gi.workload_inputs("decode")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    dq, dk, dv, dg, db = (up(dinp[n]) for n in ("q", "k", "v", "g", "beta"))
+    st0 = up(dinp["state"])
+    nsteps = min(nsteps, D["T"])
+    toks = [tuple(t[:, i].contiguous() for t in (dq, dk, dv, dg, db)) for i in range(nsteps)]
+    ys = [torch.empty((D["B"], D["Hv"], D["Dv"]), dtype=torch.float16, device=dev) for _ in range(nsteps)]
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if kind == "inplace":
+        st = st0.clone()
+        for i in range(nsteps):                  # warm-up pass
+            gdn.step(*toks[i], st, state_out=st, y=ys[i], stream=stream)
+        st.copy_(st0)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(nsteps):
+            gdn.step(*toks[i], st, state_out=st, y=ys[i], stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / nsteps
+    else:
+        scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        sa, sb = st0.clone(), torch.empty_like(st0)
+        tot = 0.0
+        for i in range(nsteps):
+            scratch.sum()
+            ev0.record(stream)
+            gdn.step(*toks[i], sa, state_out=sb, y=ys[i], stream=stream)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            tot += ev0.elapsed_time(ev1)
+            sa, sb = sb, sa
+        us = tot * 1e3 / nsteps
+    sbytes, tbytes = step_bytes(**D)
+    print(json.dumps({"decode_only": kind, "steps": nsteps, "us_per_step": us,
+                      "total_GBps": tbytes / (us * 1e-6) / 1e9,
+                      "frac": tbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
+
+
 def copy_calibration(mib: int):
     import torch
     n = mib * 1024 * 1024 // 4
@@ -191,9 +293,17 @@ def main():
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
+    ap.add_argument("--decode-only", choices=["inplace", "flushed"],
+                    help="run only the decode loop of that kind (for counter collection)")
+    ap.add_argument("--summarize-step-traffic", nargs=5, metavar=("KIND", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="summarise FETCH_SIZE / WRITE_SIZE of the decode step kernel for a "
+                         "--decode-only KIND run")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_step_traffic:
+        summarize_step_traffic(*args.summarize_step_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
@@ -202,6 +312,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.decode_only:
+        decode_only(args.decode_only, args.decode_steps)
         return
 
     import numpy as np
@@ -507,11 +620,25 @@ def main():
         t0 = time.perf_counter()
         oracle.forward(qs, ks, vs, gs, bs, ss, nthreads=nthreads)
         cpu_s = time.perf_counter() - t0
+        # the three small prefill workloads on one thread each
+        single = []
+        for name in ("tiny_f32", "bonsai_prefill", "gqa_ragged"):
+            W = gi.WORKLOADS[name]
+            winp = gi.workload_inputs(name)
+            wq, wk, wv = (gi.decode(winp[n], W["dtype"]) for n in ("q", "k", "v"))
+            ws = winp["state"].astype(np.float64) if winp["state"] is not None else None
+            t1 = time.perf_counter()
+            oracle.forward(wq, wk, wv, winp["g"].astype(np.float64), winp["beta"].astype(np.float64),
+                           ws, nthreads=1)
+            sec = time.perf_counter() - t1
+            single.append({"workload": name, "threads": 1, "seconds": sec,
+                           "tokens_per_s": W["B"] * W["T"] / sec})
         out["cpu_baseline"] = {
             "value": nb * P["T"] / cpu_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"the whole long prefill, {nb} x {P['T']} tokens x {P['Hv']} value heads "
                       f"(float64 sequential rule, OpenMP over (batch, head) slots), {cpu_s:.2f} s "
                       f"on {nthreads} threads",
+            "single_thread": single,
         }
     print(json.dumps(out), flush=True)
 
