@@ -65,11 +65,11 @@ BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, TFLOP/s
 F32_PEAK_TFLOPS = 157.3          # MI355X dense fp32 MFMA, TFLOP/s
 PREFILL = dict(B=8, T=8192, Hk=16, Hv=32, Dk=128, Dv=128, C=64, dtype="bf16")
 DECODE = dict(B=64, T=256, Hk=16, Hv=32, Dk=128, Dv=128, dtype="f16")
-CHUNK_KERNEL_SOURCES = ["gdn_chunk_pipe.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_internal.h",
+CHUNK_KERNEL_SOURCES = ["gdn_chunk_wy.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h", "gdn_internal.h",
                         "gdn_device.h", "gdn_chunk_bf16.hip"]
 # the kernel that runs the long-prefill workload (bf16, Dk = Dv = 128, C = 64)
-CHUNK_KERNEL = "chunk_pipe_kernel"
-CHUNK_KERNEL_LABEL = "chunk_pipe_kernel<bf16,128,128,64>"
+CHUNK_KERNEL = "chunk_wy_kernel"
+CHUNK_KERNEL_LABEL = "chunk_wy_kernel<bf16> (Dk=Dv=128, C=64)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_long_prefill_hbm_traffic.json")
 
 

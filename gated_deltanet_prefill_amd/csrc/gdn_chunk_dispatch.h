@@ -2,7 +2,7 @@
 #pragma once
 
 #include "gdn_chunk_impl.h"
-#include "gdn_chunk_pipe.h"
+#include "gdn_chunk_wy.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -51,7 +51,7 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
     if constexpr (sizeof(ET) == 2 && DK == 128 && DV == 128 && C == 64) {
         // the pipelined kernel: one 8-wave workgroup per slot
         const int xcd_group = (group > 1 && nslots % (8L * group) == 0) ? group : 1;
-        hipLaunchKernelGGL((chunk_pipe_kernel<ET, DK, DV, C>), dim3((unsigned)nslots), dim3(512), 0, st,
+        hipLaunchKernelGGL((chunk_wy_kernel<ET>), dim3((unsigned)nslots), dim3(512), 0, st,
                            static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                            static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                            static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale, a.flags);

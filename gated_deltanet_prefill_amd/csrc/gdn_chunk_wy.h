@@ -1,0 +1,810 @@
+// gdn_chunk_wy.h -- the pipelined chunk kernel for gfx950: 16-bit q/k/v/y,
+// Dk = Dv = 128, chunks of 64 tokens, the chunk's triangular system inverted
+// in float32.
+//
+// Per chunk, in the compact WY form of the metaltile-std gated_delta_wy.rs
+// page (module notes, "Algorithm", steps 4-9: one unit lower triangular
+// solve turns the chunk's keys and values into pseudo-keys and pseudo-values,
+// and the state enters only through products with them), with the decay
+// products of the ferrox-core gdn_chunk.rs page ("The algebra": every ratio
+// of decays is a product of decays):
+//
+//   A[t][j]   = beta_t R[t][j] k_t.k_j  (j < t),   T = (I + A)^-1
+//   W         = T diag(beta G) K,   U = T diag(beta) V            (state free)
+//   QKR[t][j] = R[t][j] q_t.k_j / sqrt(Dk)  (j <= t)
+//   D         = U - W S^T            the true deltas d_t of the chunk
+//   y         = G (Q S^T) / sqrt(Dk) + QKR D
+//   S        <- G_last S + (diag(Rl) D)^T K,   Rl[t] = R[c-1][t]
+//
+// The triangular system is solved in float32 (the metaltile page's
+// "Numerical precision": float32 is the floor for the solves):
+//
+//  * the 16x16 diagonal blocks T_ii = (I + A_ii)^-1 by float32 forward
+//    substitution on the vector ALUs;
+//  * the blocks below the diagonal column by column,
+//      T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
+//    every product a float32 matrix-core product (v_mfma_f32_16x16x4_f32:
+//    float32 operands, products and accumulation);
+//  * W and U as products of T with the exact 16-bit K and V, T carried as a
+//    two-term expansion T = T_h + T_l (16 significant bits, relative error
+//    <= 2^-17): [T_h | T_l] times [K ; K] is one 16x16x32 MFMA per block.
+//    W is then rounded once to the 16-bit operand of W S^T; U stays float32
+//    and starts the accumulation of D.
+//
+// One workgroup of eight waves owns one (batch, value head) slot.  Waves 0-3
+// (state waves) keep the float32 state in registers, 32 value rows each;
+// waves 4-7 (prep waves) build the state-free matrices one chunk ahead and
+// load the inputs.  Each SIMD holds one wave of each kind.  Iteration n has
+// two phases, each closed by a workgroup barrier:
+//
+//   phase a  state: Y = Q_n S^T, the Q K^T tiles of chunk n -> QKR,
+//                   U_n = T_n diag(beta) V_n (the start of D)
+//            prep:  -W_n = -T_n diag(beta G) K_n; K K^T tiles of chunk n+1
+//                   -> A, the diagonal inverses T_ii;  load K_{n+2}
+//   phase b  state: D = U_n - W_n S^T, y = G Y / sqrt(Dk) + QKR D, state
+//                   update
+//            prep:  the blocks of T_{n+1} below the diagonal and its scaled
+//                   expansions; gate products of chunk n+2; load Q_{n+1},
+//                   V_{n+1}
+//
+// LDS layouts.  K, Q and -W have 256-byte token rows (keys along the row);
+// the 16-byte unit u of row t sits at u ^ (t % 16).  QKR has 128-byte rows,
+// unit u of row t at u ^ ((t / 2) % 8), and column j = 32 s + 16 h + 4 q + r
+// at position 32 s + 8 q + 4 h + r.  Float32 16x16 blocks (A below the
+// diagonal, T_ii by rows and by columns) have 64-byte rows, unit u of row r
+// at u ^ ((r / 4) % 4).  The expansions of T diag(beta G) and T diag(beta)
+// are stored block by block transposed (row c holds column c of the block),
+// 32-byte rows with the 8-byte piece s of row c at s ^ (2 (c / 8)), and read
+// back as row fragments with gfx950's LDS transpose load.
+//
+// Lane x of value tile vb of state wave w holds value column
+//   32 w + 8 (x/4) + 4 vb + x%4;
+// row 4 qd + r of key tile kb = 2 s + h of the state holds key
+//   32 s + 8 qd + 4 h + r,
+// so that the -W, Q and K row fragments of a 32-key step are single 16-byte
+// reads of eight consecutive keys.
+#pragma once
+
+#include <type_traits>
+
+#include "gdn_chunk_impl.h"
+
+namespace gdn {
+
+template <typename ET>
+struct WyCfg {
+    static_assert(sizeof(ET) == 2, "16-bit element types only");
+    static constexpr int C = 64, DK = 128, DV = 128;
+    static constexpr int NBT = C / 16;        // 16-token blocks
+    static constexpr int NBK = DK / 16;       // 16-key blocks
+    static constexpr int NSK = DK / 32;       // contraction steps over keys
+    static constexpr int NB = 2;              // value tiles per state wave
+    static constexpr unsigned KBUF = C * DK * 2;          // one chunk of K, Q or -W
+    static constexpr unsigned oK = 0;                     // 3 x K
+    static constexpr unsigned oQ = oK + 3 * KBUF;         // Q
+    static constexpr unsigned VSL = C * 32 * 2;           // one 32-column V slice
+    static constexpr unsigned oV = oQ + KBUF;             // 4 x V slice [C][32]
+    static constexpr unsigned oW = oV + 4 * VSL;          // -W
+    static constexpr unsigned oQKR = oW + KBUF;           // QKR [C][C]
+    static constexpr unsigned FBLK = 16 * 16 * 4;         // one float32 16x16 block
+    static constexpr unsigned oA = oQKR + C * C * 2;      // -A below the diagonal: 6 blocks
+    static constexpr unsigned oTd = oA + 6 * FBLK;        // T_ii by rows
+    static constexpr unsigned oTdT = oTd + 4 * FBLK;      // T_ii by columns
+    static constexpr unsigned LDD = 20;                   // floats per row of Ad
+    static constexpr unsigned oAd = oTdT + 4 * FBLK;      // A_ii [C][LDD]
+    static constexpr unsigned HBLK = 16 * 16 * 2;         // one 16-bit 16x16 block
+    static constexpr unsigned oTW = oAd + C * LDD * 4;    // -T diag(beta G): 10 blocks x (hi, lo)
+    static constexpr unsigned oTU = oTW + 20 * HBLK;      // T diag(beta): 10 blocks x (hi, lo)
+    static constexpr unsigned NV = 7 * C;                 // floats per gate-vector set
+    static constexpr unsigned oVec = oTU + 20 * HBLK;     // 3 gate-vector sets
+    static constexpr unsigned oGB = oVec + 3 * NV * 4;    // g, beta of two chunks, as loaded
+    static constexpr unsigned BYTES = oGB + 2 * 2 * C * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Gate-vector set of one chunk (floats): beta, g, in-block inclusive prefix
+// products P, in-block exclusive suffix products Sfx, G, Rl, block totals.
+enum { kVb = 0, kVg = 1, kVP = 2, kVSfx = 3, kVG = 4, kVRl = 5, kVBT = 6 };
+
+// Four 16-bit elements through gfx950's LDS transpose read: lane m of each
+// 16-lane group receives element m%4 of the 8-byte pieces addressed by lanes
+// m/4 + 4i, i = 0..3.  With lane j addressing row r0 + j/4 at column
+// c(j%4) .. +3, lane m receives column c(m/4) + m%4 of rows r0 .. r0+3.
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x4 ld_tr(const char *smem, unsigned byte) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(smem + byte));
+    return __builtin_bit_cast(typename Vec<ET>::x4, raw);
+}
+template <typename ET>
+__device__ __forceinline__ typename Vec<ET>::x8 lds8(const char *smem, unsigned byte) {
+    return *reinterpret_cast<const typename Vec<ET>::x8 *>(smem + byte);
+}
+template <typename ET>
+__device__ __forceinline__ void sts4(char *smem, unsigned byte, typename Vec<ET>::x4 v) {
+    *reinterpret_cast<typename Vec<ET>::x4 *>(smem + byte) = v;
+}
+
+// acc += a b for one 16x16x16 block in float32 (four v_mfma_f32_16x16x4_f32,
+// float32 products and accumulation); a and b are float32 fragments (lane
+// (x, qd) holds contraction indices 4 qd .. 4 qd + 3 of row / column x).
+__device__ __forceinline__ f32x4 mma_f32(f32x4 a, f32x4 b, f32x4 acc) {
+    acc = mfma(a[0], b[0], acc);
+    acc = mfma(a[1], b[1], acc);
+    acc = mfma(a[2], b[2], acc);
+    acc = mfma(a[3], b[3], acc);
+    return acc;
+}
+
+// The C x C tiles of K K^T (prep waves) or Q K^T (state waves) that wave w
+// of a kind computes: tile i has token block ib (rows t of the result) and
+// key block jb (columns j), ib >= jb; tile 0 is the diagonal tile (w, w).
+//   w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
+//   w = 2: (2,2) (3,2)         w = 3: (3,3) (3,0)
+constexpr int wy_ntiles(int w) { return w < 2 ? 3 : 2; }
+constexpr int wy_tile_ib(int w, int i) { return w == 0 ? i : w == 1 ? 1 + i : w == 2 ? 2 + i : 3; }
+constexpr int wy_tile_jb(int w, int i) { return w == 3 ? (i == 0 ? 3 : 0) : w; }
+// index of block (i, j), i > j, among the six blocks below the diagonal
+constexpr int wy_aidx(int i, int j) { return i * (i - 1) / 2 + j; }
+// index of block (i, j), i >= j, among the ten blocks of the lower triangle
+constexpr int wy_tidx(int i, int j) { return i * (i + 1) / 2 + j; }
+
+template <typename ET>
+__global__ __launch_bounds__(512, 1)
+void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
+                     const ET *__restrict__ v, const float *__restrict__ g,
+                     const float *__restrict__ beta, const float *state_in,
+                     float *state_out, ET *__restrict__ y,
+                     int T, int Hk, int Hv, int xcd_group, float scale, int flags)
+{
+    using L = WyCfg<ET>;
+    using X4 = typename Vec<ET>::x4;
+    using X8 = typename Vec<ET>::x8;
+    constexpr int C = L::C, DK = L::DK, DV = L::DV;
+    constexpr int NBT = L::NBT, NBK = L::NBK, NSK = L::NSK, NB = L::NB;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    auto Gv = [&](int c) { return reinterpret_cast<float *>(smem + L::oVec + (c % 3) * L::NV * 4); };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wave & 3;                      // state wave index, or prep wave index
+    const bool state_wave = wave < 4;
+    // Lane coordinates.  They pass through an empty asm statement at the top
+    // of every chunk, so the compiler forms lane-dependent addresses inside
+    // the loop instead of holding dozens of precombined addresses across it.
+    int lane = tid & 63, x = lane & 15, qd = lane >> 4;
+
+    // Workgroups are dealt round-robin over the 8 XCDs, so workgroups i and
+    // i + 8 share an XCD and its L2; with xcd_group = Hv/Hk > 1 they get
+    // value heads of the same key head, whose q/k stream is then fetched
+    // from HBM once per group.
+    int bid = blockIdx.x;
+    if (xcd_group > 1) {
+        const int xcd = bid & 7, kk = bid >> 3;
+        const int sib = kk % xcd_group, mm = kk / xcd_group;
+        bid = (mm * 8 + xcd) * xcd_group + sib;
+    }
+    const int b = bid / Hv, hv = value_head_of_rank(bid % Hv, Hk, Hv, flags);
+    const int hk = key_head(hv, Hk, Hv, flags);
+    const int nchunks = (T + C - 1) / C;
+
+    // ---- lane-dependent LDS byte offsets
+    // K/Q/-W row fragment (16 bytes at unit 4 s + qd of row 16 b + x): ^ 64 s, + 4096 b
+    auto f_lKt = [&]() { return (unsigned)(x * 256 + (((qd ^ x) & 15) << 4)); };
+    // K transpose read, rows 16 jb + 4 qd + x/4, keys 16 kt + 4 (x%4) ..: ^ 32 kt, + 4096 jb
+    auto f_lKtr = [&]() {
+        const int r4 = 4 * qd + (x >> 2);
+        return (unsigned)(r4 * 256 + (((((x >> 1) & 1) ^ r4) & 15) << 4) + ((x & 1) << 3));
+    };
+    // K transpose read for the state update, rows r0 + r4, keys 32 s + 4 h +
+    // 8 (x%4) .. +3 (lane x then receives key 32 s + 4 h + 8 (x/4) + x%4):
+    // ^ 64 s, + 8 h, + 256 r0
+    auto f_lKu = [&]() {
+        const int r4 = 4 * qd + (x >> 2);
+        return (unsigned)(r4 * 256 + ((((x & 3) ^ r4) & 15) << 4));
+    };
+    // -W write: token 16 ib + x, keys 16 kt + 4 qd .. + 3: ^ 32 kt, + 4096 ib
+    auto f_lWp = [&]() { return (unsigned)(x * 256 + ((((qd >> 1) ^ x) & 15) << 4) + 8 * (qd & 1)); };
+    // QKR rows 16 tb + x, the 4 columns 16 jb + 4 qd ..: (this ^ 64 (jb/2)) +
+    // 8 (jb%2) + 2048 tb; the 8 columns of blocks 2 s, 2 s + 1: ^ 64 s
+    auto f_lA = [&]() { return (unsigned)(x * 128 + (((qd ^ (x >> 1)) & 7) << 4)); };
+    auto aoff = [](unsigned lA, int jb, int tb) { return (lA ^ (64 * (jb >> 1))) + 8 * (jb & 1) + 2048 * tb; };
+    // V slice: transpose read rows 16 jb + r4, permuted columns 8 (m/4) + 4 vb + m%4: + 8 vb + 1024 jb
+    auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 64 + (x & 3) * 16); };
+    // float32 block, row fragment of row x (unit qd)
+    auto f_lF = [&]() { return (unsigned)(x * 64 + ((qd ^ ((x >> 2) & 3)) << 4)); };
+    // transposed 16-bit block of T: transpose read giving lane (x, qd) the
+    // row-x entries of columns 4 qd .. 4 qd + 3
+    auto f_lT = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 32 + 8 * ((x & 3) ^ ((qd >> 1) << 1))); };
+
+    // ---------------- input loads (prep waves) ----------------
+    // Chunks of K, Q and V go from global memory straight into LDS
+    // (global_load_lds_dwordx4: lane l of the wave writes the 16 bytes at
+    // 16 l of a 1 KB block), written as inline assembly so that the compiler
+    // does not wait for the transfer before the wave's next LDS access; the
+    // prep waves, which issue no other global memory operations, await them
+    // with s_waitcnt vmcnt(0) before the barrier that closes phase b.  Prep
+    // wave p fills K/Q rows 16 p .. 16 p + 15 and the V columns 32 p .. 32 p
+    // + 31.  The swizzle of K and Q is applied on the source side.  Rows past
+    // the end of the sequence fetch the last row again; with g = 1 and
+    // beta = 0 there, those rows add nothing (A, W, U and D vanish on them,
+    // and their y rows are not stored).
+    const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * DV;
+    const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
+    const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
+    const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV;
+    const float *gbase = g + (size_t)b * T * Hv + hv;
+    const float *bbase = beta + (size_t)b * T * Hv + hv;
+    auto f_okq0 = [&](int rg) { return (unsigned)((16 * rg + qd) * kstride + 8 * ((lane & 15) ^ qd)); };
+    auto f_ov0 = [&]() { return (unsigned)((lane >> 2) * vstride + 8 * (lane & 3)); };
+    const unsigned lds_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
+    auto g2lds = [&](const ET *src, unsigned off, unsigned lds_byte) {
+        const unsigned la = __builtin_amdgcn_readfirstlane(lds_base + lds_byte);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(src), "s"(la) : "memory", "m0");
+#pragma clang diagnostic pop
+    };
+    // rows 16 rg .. 16 rg + 15 of a K or Q chunk
+    auto issue_kq = [&](const ET *base, unsigned dst, int c, int rg) {
+        const int t0 = c * C;
+        const ET *src = base + (size_t)t0 * kstride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (t0 + C <= T) {
+                g2lds(src, 2 * ((f_okq0(rg) ^ (32 * i)) + 4 * i * (unsigned)kstride), dst + 4096 * rg + 1024 * i);
+            } else {
+                const int r = 16 * rg + 4 * i + (lane >> 4);
+                g2lds(src, 2 * (unsigned)(min(r, T - t0 - 1) * kstride + 8 * ((lane & 15) ^ (r & 15))),
+                      dst + 4096 * rg + 1024 * i);
+            }
+        }
+    };
+    // value columns 32 sl .. 32 sl + 31 of a V chunk
+    auto issue_v = [&](int c, int sl) {
+        const int t0 = c * C;
+        const ET *src = vbase + (size_t)t0 * vstride + 32 * sl;
+        const unsigned dst = L::oV + sl * L::VSL;
+        if (t0 + C <= T) {
+            const unsigned o0 = f_ov0();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g2lds(src, 2 * (o0 + 16 * i * (unsigned)vstride), dst + 1024 * i);
+        } else {
+            const int last = T - t0 - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                g2lds(src, 2 * (unsigned)(min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3)), dst + 1024 * i);
+        }
+    };
+    // g and beta of chunk c into the staging buffer c % 2 (one wave; lane =
+    // token, rows past the end read the last row)
+    auto load_gb = [&](int c) {
+        const int t0 = c * C;
+        const unsigned off = 4 * (unsigned)(min(lane, T - t0 - 1) * Hv);
+        const float *gc = gbase + (size_t)t0 * Hv, *bc = bbase + (size_t)t0 * Hv;
+        const unsigned gbo = L::oGB + (unsigned)(c & 1) * 2 * C * 4;
+        const unsigned lg = __builtin_amdgcn_readfirstlane(lds_base + gbo);
+        const unsigned lb = __builtin_amdgcn_readfirstlane(lds_base + gbo + C * 4);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     :: "v"(off), "s"(gc), "s"(lg) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     :: "v"(off), "s"(bc), "s"(lb) : "memory", "m0");
+#pragma clang diagnostic pop
+    };
+    // Gate products of chunk c (one wave, lane t holding g_t; g = 1 and
+    // beta = 0 past the end): within each 16-token block (one DPP row) the
+    // inclusive prefix products P and the inclusive suffix products by four
+    // doubling steps; the exclusive suffix Sfx; block totals; G[t] = P[t] x
+    // totals of the earlier blocks; Rl[t] = Sfx[t] x totals of the later
+    // blocks.  Every ratio of decays used later is a product of these.
+    auto scan_gates = [&](int c) {
+        const float *gb = reinterpret_cast<const float *>(smem + L::oGB + (c & 1) * 2 * C * 4);
+        const float rg = gb[lane];
+        const float rb = gb[C + lane];
+        const int cn = min(C, T - c * C);
+        float *gv = Gv(c);
+        const float gt = lane < cn ? decay_of(rg, flags) : 1.f;
+        float p = gt, sx = gt;
+        p *= dpp_row_shr<1>(p);
+        p *= dpp_row_shr<2>(p);
+        p *= dpp_row_shr<4>(p);
+        p *= dpp_row_shr<8>(p);
+        sx *= dpp_row_shl<1>(sx);
+        sx *= dpp_row_shl<2>(sx);
+        sx *= dpp_row_shl<4>(sx);
+        sx *= dpp_row_shl<8>(sx);
+        const float sfx = dpp_row_shl<1>(sx);
+        const int bt = lane >> 4;
+        float gpre = p, rl = sfx;
+#pragma unroll
+        for (int bb = 0; bb < NBT; ++bb) {
+            const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 16 * bb + 15));
+            if (bb < bt) gpre *= tot;
+            if (bb > bt) rl *= tot;
+            if (lane == bb) gv[kVBT * C + bb] = tot;
+        }
+        gv[kVb * C + lane] = lane < cn ? rb : 0.f;
+        gv[kVg * C + lane] = gt;
+        gv[kVP * C + lane] = p;
+        gv[kVSfx * C + lane] = sfx;
+        gv[kVG * C + lane] = gpre;
+        gv[kVRl * C + lane] = rl;
+    };
+    static_assert(C == 64, "one lane per token in the gate scans");
+
+    // ---- decay ratios of tile i of wave `wk` (token block ib, key block jb)
+    // for lane (x, qd): t = 16 ib + x, j = 16 jb + 4 qd + r.
+    // Diagonal tile: R[t][j] = g_{j+1} ... g_t (j <= t) by an inclusive scan
+    // of g over the 16 lanes x of a DPP row, starting after 4 qd + 3.
+    auto diag_ratio = [&](const float *gv, int blk) {
+        const float gx = gv[kVg * C + 16 * blk + x];
+        float h = (x >= 4 * qd + 4) ? gx : 1.f;
+        h *= dpp_row_shr<1>(h);
+        h *= dpp_row_shr<2>(h);
+        h *= dpp_row_shr<4>(h);
+        h *= dpp_row_shr<8>(h);
+        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gv + kVg * C + 16 * blk + 4 * qd);
+        f32x4 R;
+        R[3] = h;
+        R[2] = (4 * qd + 3 <= x) ? R[3] * g4[3] : 1.f;
+        R[1] = (4 * qd + 2 <= x) ? R[2] * g4[2] : 1.f;
+        R[0] = (4 * qd + 1 <= x) ? R[1] * g4[1] : 1.f;
+        return R;
+    };
+    // Below the diagonal: R[t][j] = P[t] x (totals of the blocks strictly
+    // between) x Sfx[j].
+    auto off_ratio = [&](const float *gv, int ib, int jb) {
+        float mf = gv[kVP * C + 16 * ib + x];
+#pragma unroll
+        for (int bb = 1; bb < NBT - 1; ++bb) mf *= (bb > jb && bb < ib) ? gv[kVBT * C + bb] : 1.f;
+        return *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * jb + 4 * qd) * mf;
+    };
+
+    if (state_wave) {
+        // ================= state waves =================
+        f32x4 S[NBK][NB];                        // S^T tiles: rows = keys kcol, columns = values
+        const size_t sbase = ((size_t)b * Hv + hv) * DV * DK;
+        auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
+        auto kcol = [&](int kb, int q4) { return 32 * (kb >> 1) + 8 * q4 + 4 * (kb & 1); };
+        {
+            // rows of zeros (stride 0) when there is no initial state
+            gfloat *sin = state_in ? (gfloat *)state_in + sbase : (gfloat *)kZeroRow;
+            const size_t rstride = state_in ? DK : 0;
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+                for (int kb = 0; kb < NBK; ++kb)
+                    S[kb][vb] = *reinterpret_cast<gf32x4 *>(sin + (size_t)vcol(vb, x) * rstride + kcol(kb, qd));
+        }
+        // QKR blocks above the diagonal are never written: zero the buffer once.
+        for (int i = tid; i < (int)(C * C * 2 / 16); i += 256)
+            reinterpret_cast<uint4 *>(smem + L::oQKR)[i] = zero_u4();
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+        // K of chunk 0, the gates of chunks 0 and 1 and the gate products
+        // of chunk 0 before the pipeline starts
+        if (nchunks > 0) {
+            issue_kq(kbase, L::oK, 0, w);
+            if (w == 0) {
+                load_gb(0);
+                if (nchunks > 1) load_gb(1);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (w == 0 && nchunks > 0) scan_gates(0);
+        lds_barrier();
+        // The state waves load K two chunks ahead and the gates three ahead,
+        // at the start of phase a (they would otherwise wait at its end), and
+        // wait for them before its barrier.
+        auto issue_inputs = [&](int n) {
+            if (n + 2 < nchunks) issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, w);
+            if (w == 0 && n + 3 < nchunks) load_gb(n + 3);
+        };
+        issue_inputs(-1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();                           // A, T_ii of chunk 0
+        lds_barrier();                           // T of chunk 0, Q_0, V_0
+        for (int n = 0; n < nchunks; ++n) {
+            asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
+            issue_inputs(n);
+            const unsigned lKt = f_lKt(), lA = f_lA();
+            const unsigned kbn = L::oK + (n % 3) * L::KBUF;
+            const float *gv = Gv(n);
+            f32x4 D[NBT][NB], Y[NB][NBT];
+            // ---------------- phase a ----------------
+            {
+                // Y^T = S Q^T, and this wave's Q K^T tiles from the same Q fragments
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = zero4();
+                auto qk_tiles = [&](auto W) {
+                    constexpr int wc = decltype(W)::value;
+                    constexpr int nt = wy_ntiles(wc);
+                    f32x4 acc[nt];
+#pragma unroll
+                    for (int i = 0; i < nt; ++i) acc[i] = zero4();
+#pragma unroll
+                    for (int s = 0; s < NSK; ++s) {
+                        const unsigned lo = lKt ^ (64 * s);
+                        X8 fs[NB];
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
+                        X8 fq[NBT];
+#pragma unroll
+                        for (int tb = 0; tb < NBT; ++tb) fq[tb] = lds8<ET>(smem, L::oQ + lo + 4096 * tb);
+#pragma unroll
+                        for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                            for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = mfma(fs[vb], fq[tb], Y[vb][tb]);
+#pragma unroll
+                        for (int i = 0; i < nt; ++i) {
+                            const X8 fk = lds8<ET>(smem, kbn + lo + 4096 * wy_tile_jb(wc, i));
+                            acc[i] = mfma(fk, fq[wy_tile_ib(wc, i)], acc[i]);
+                        }
+                    }
+                    // QKR = R (Q K^T) / sqrt(Dk), lower including the diagonal
+                    {
+                        const f32x4 R = diag_ratio(gv, wc);
+                        f32x4 o;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[0][r]) : 0.f;
+                        sts4<ET>(smem, L::oQKR + aoff(lA, wc, wc), cvt4<ET>(o));
+                    }
+#pragma unroll
+                    for (int i = 1; i < nt; ++i) {
+                        const int ib = wy_tile_ib(wc, i), jb = wy_tile_jb(wc, i);
+                        const f32x4 R = off_ratio(gv, ib, jb);
+                        sts4<ET>(smem, L::oQKR + aoff(lA, jb, ib), cvt4<ET>(R * acc[i] * scale));
+                    }
+                };
+                switch (w) {
+                case 0: qk_tiles(std::integral_constant<int, 0>{}); break;
+                case 1: qk_tiles(std::integral_constant<int, 1>{}); break;
+                case 2: qk_tiles(std::integral_constant<int, 2>{}); break;
+                default: qk_tiles(std::integral_constant<int, 3>{}); break;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                // U = T diag(beta) V for this wave's value columns: the
+                // start of D.  [T_h | T_l] [V ; V] per block, V read with the
+                // permuted columns of the value tiles.
+                const unsigned vsl = L::oV + w * L::VSL + f_lVs(), lT = f_lT();
+                X4 vc[NBT][NB];
+#pragma unroll
+                for (int jb = 0; jb < NBT; ++jb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) vc[jb][vb] = ld_tr<ET>(smem, vsl + 8 * vb + 1024 * jb);
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) D[tb][vb] = zero4();
+#pragma unroll
+                    for (int jb = 0; jb <= tb; ++jb) {
+                        const unsigned to = L::oTU + 2 * wy_tidx(tb, jb) * L::HBLK + lT;
+                        const X8 ft = cat8<ET>(ld_tr<ET>(smem, to), ld_tr<ET>(smem, to + L::HBLK));
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            D[tb][vb] = mfma(ft, cat8<ET>(vc[jb][vb], vc[jb][vb]), D[tb][vb]);
+                    }
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            // ---------------- phase b ----------------
+            // The state's 16-bit operands are formed again here rather than
+            // kept from phase a (32 registers fewer across the barrier).
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
+            {
+                // D = U + (-W) S^T
+#pragma unroll
+                for (int s = 0; s < NSK; ++s) {
+                    X8 fs[NB];
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb)
+                        fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
+#pragma unroll
+                    for (int tb = 0; tb < NBT; ++tb) {
+                        const X8 fw = lds8<ET>(smem, L::oW + (lKt ^ (64 * s)) + 4096 * tb);
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb) D[tb][vb] = mfma(fw, fs[vb], D[tb][vb]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // Y^T = G (S Q^T) / sqrt(Dk) + D^T QKR^T
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    const float gt = gv[kVG * C + 16 * tb + x] * scale;
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Y[vb][tb] *= gt;
+                }
+                X4 Df[NBT][NB];
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb)
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Df[tb][vb] = cvt4<ET>(D[tb][vb]);
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    // QKR is zero above the diagonal blocks: pair blocks (0,1), (2,3)
+#pragma unroll
+                    for (int s = 0; 2 * s <= tb; ++s) {
+                        const X8 fr = lds8<ET>(smem, L::oQKR + (lA ^ (64 * s)) + 2048 * tb);
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            Y[vb][tb] = mfma(cat8<ET>(Df[2 * s][vb], Df[2 * s + 1][vb]), fr, Y[vb][tb]);
+                    }
+                }
+                // y: lane (x, qd) holds token 16 tb + x, values 32 w + 8 qd + (0..7).
+                // The stores go through a buffer resource that spans the
+                // chunk's cn valid token rows: the hardware drops those past
+                // the end of the sequence, with no branch around the stores.
+                {
+                    typedef int i32x4 __attribute__((ext_vector_type(4)));
+                    const int t0 = n * C, cn = min(C, T - t0);
+                    const unsigned rowb = (unsigned)(Hv * DV) * (unsigned)sizeof(ET);
+                    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(y + (((size_t)b * T + t0) * Hv + hv) * DV), (short)0, (int)(cn * rowb), 0x00020000);
+#pragma unroll
+                    for (int tb = 0; tb < NBT; ++tb)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(i32x4, cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]))), yr,
+                            (int)((16 * tb + x) * rowb + (32 * w + 8 * qd) * sizeof(ET)), 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // S^T <- G_last S^T + K^T diag(Rl) D
+                const unsigned lKu = f_lKu();
+                X4 Dp[NBT][NB];
+#pragma unroll
+                for (int tb = 0; tb < NBT; ++tb) {
+                    const f32x4 rl = *reinterpret_cast<const f32x4 *>(gv + kVRl * C + 16 * tb + 4 * qd);
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) Dp[tb][vb] = cvt4<ET>(D[tb][vb] * rl);
+                }
+                const float glast = gv[kVG * C + C - 1];
+#pragma unroll
+                for (int kb = 0; kb < NBK; ++kb) {
+                    X8 fk[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const unsigned ka = kbn + (lKu ^ (64 * (kb >> 1))) + 8 * (kb & 1) + 256 * 32 * s;
+                        fk[s] = cat8<ET>(ld_tr<ET>(smem, ka), ld_tr<ET>(smem, ka + 256 * 16));
+                    }
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) S[kb][vb] *= glast;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int vb = 0; vb < NB; ++vb)
+                            S[kb][vb] = mfma(fk[s], cat8<ET>(Dp[2 * s][vb], Dp[2 * s + 1][vb]), S[kb][vb]);
+                }
+            }
+            lds_barrier();
+        }
+        // ---- the state, written once
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb)
+                *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)vcol(vb, x) * DK + kcol(kb, qd)) = S[kb][vb];
+    } else {
+        // ================= prep waves =================
+        const int p = w;
+        lds_barrier();
+        // iteration n: phase a builds -W of chunk n and A, T_ii of chunk n+1;
+        // phase b the rest of T of chunk n+1 (n = -1 is the pipeline's start)
+        for (int n = -1; n < nchunks; ++n) {
+            asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
+            const int m = n + 1;
+            // ---------------- phase a ----------------
+            if (n >= 0) {
+                // -W^T = K^T (-T diag(beta G))^T for key tiles 2 p, 2 p + 1:
+                // lane (x, qd) of tile (kt, ib) holds keys 16 kt + 4 qd .. + 3
+                // of token 16 ib + x, one 8-byte write into the token rows of -W.
+                const unsigned kbn = L::oK + (n % 3) * L::KBUF;
+                const unsigned lKtr = f_lKtr(), lT = f_lT(), lWp = f_lWp();
+                X4 kc[NBT][2];
+#pragma unroll
+                for (int jb = 0; jb < NBT; ++jb)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) kc[jb][c] = ld_tr<ET>(smem, kbn + (lKtr ^ (32 * (2 * p + c))) + 4096 * jb);
+                X8 ft[NBT * (NBT + 1) / 2];
+#pragma unroll
+                for (int ib = 0; ib < NBT; ++ib)
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb) {
+                        const unsigned to = L::oTW + 2 * wy_tidx(ib, jb) * L::HBLK + lT;
+                        ft[wy_tidx(ib, jb)] = cat8<ET>(ld_tr<ET>(smem, to), ld_tr<ET>(smem, to + L::HBLK));
+                    }
+                f32x4 acc[NBT][2];
+#pragma unroll
+                for (int ib = 0; ib < NBT; ++ib)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        acc[ib][c] = zero4();
+#pragma unroll
+                        for (int jb = 0; jb <= ib; ++jb)
+                            acc[ib][c] = mfma(cat8<ET>(kc[jb][c], kc[jb][c]), ft[wy_tidx(ib, jb)], acc[ib][c]);
+                    }
+#pragma unroll
+                for (int ib = 0; ib < NBT; ++ib)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        sts4<ET>(smem, L::oW + (lWp ^ (32 * (2 * p + c))) + 4096 * ib, cvt4<ET>(acc[ib][c]));
+            }
+            if (m < nchunks) {
+                // K K^T tiles of chunk m -> A (float32): the diagonal tile to
+                // Ad (for the inverse), the tiles below it to their blocks
+                const unsigned kbm = L::oK + (m % 3) * L::KBUF;
+                const unsigned lKt = f_lKt(), lF = f_lF();
+                const float *gv = Gv(m);
+                auto kk_tiles = [&](auto W) {
+                    constexpr int wc = decltype(W)::value;
+                    constexpr int nt = wy_ntiles(wc);
+                    f32x4 acc[nt];
+#pragma unroll
+                    for (int i = 0; i < nt; ++i) acc[i] = zero4();
+#pragma unroll
+                    for (int s = 0; s < NSK; ++s) {
+                        const unsigned lo = lKt ^ (64 * s);
+#pragma unroll
+                        for (int i = 0; i < nt; ++i)
+                            acc[i] = mfma(lds8<ET>(smem, kbm + lo + 4096 * wy_tile_jb(wc, i)),
+                                          lds8<ET>(smem, kbm + lo + 4096 * wy_tile_ib(wc, i)), acc[i]);
+                    }
+                    {
+                        const int t = 16 * wc + x;
+                        const float bt = gv[kVb * C + t];
+                        const f32x4 R = diag_ratio(gv, wc);
+                        f32x4 a;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[0][r]) : 0.f;
+                        *reinterpret_cast<f32x4 *>(smem + L::oAd + (t * L::LDD + 4 * qd) * 4) = a;
+                    }
+#pragma unroll
+                    for (int i = 1; i < nt; ++i) {
+                        const int ib = wy_tile_ib(wc, i), jb = wy_tile_jb(wc, i);
+                        const f32x4 R = off_ratio(gv, ib, jb);
+                        const float bt = gv[kVb * C + 16 * ib + x];
+                        *reinterpret_cast<f32x4 *>(smem + L::oA + wy_aidx(ib, jb) * L::FBLK + lF) = R * acc[i] * (-bt);
+                    }
+                };
+                switch (p) {
+                case 0: kk_tiles(std::integral_constant<int, 0>{}); break;
+                case 1: kk_tiles(std::integral_constant<int, 1>{}); break;
+                case 2: kk_tiles(std::integral_constant<int, 2>{}); break;
+                default: kk_tiles(std::integral_constant<int, 3>{}); break;
+                }
+                // T_pp = (I + A_pp)^-1 by float32 forward substitution: four
+                // lanes per column c, lane part pt holding rows pt, pt+4,
+                // pt+8, pt+12.  Column sweep: once x_j is final (it sits in
+                // part j%4), every later row subtracts A[i][j] x_j.  The rows
+                // come from this wave's own writes above (LDS keeps a wave's
+                // accesses in order).
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                {
+                    const int base = 16 * p;
+                    const int pt = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
+                    const float *ad = reinterpret_cast<const float *>(smem + L::oAd);
+                    f32x4 arow[4][4];
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4)
+                            arow[mm][j4] = *reinterpret_cast<const f32x4 *>(ad + (base + pt + 4 * mm) * L::LDD + 4 * j4);
+                    float sv[4];
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) sv[mm] = (pt + 4 * mm == c) ? 1.f : 0.f;
+#pragma unroll
+                    for (int j = 0; j < 15; ++j) {
+                        float xj;
+                        switch (j & 3) {
+                        case 0: xj = quad_bcast<0>(sv[j >> 2]); break;
+                        case 1: xj = quad_bcast<1>(sv[j >> 2]); break;
+                        case 2: xj = quad_bcast<2>(sv[j >> 2]); break;
+                        default: xj = quad_bcast<3>(sv[j >> 2]); break;
+                        }
+#pragma unroll
+                        for (int mm = 0; mm < 4; ++mm)
+                            if (4 * mm + 3 > j) sv[mm] -= arow[mm][j >> 2][j & 3] * xj;
+                    }
+                    // rows r = pt + 4 mm of column c, into the block by rows
+                    // and the block by columns
+                    float *td = reinterpret_cast<float *>(smem + L::oTd + p * L::FBLK);
+                    float *tdt = reinterpret_cast<float *>(smem + L::oTdT + p * L::FBLK);
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const int r = pt + 4 * mm;
+                        td[r * 16 + 4 * ((c >> 2) ^ mm) + (c & 3)] = sv[mm];
+                        tdt[c * 16 + 4 * (mm ^ ((c >> 2) & 3)) + pt] = sv[mm];
+                    }
+                }
+            }
+            lds_barrier();
+            // ---------------- phase b ----------------
+            if (m < nchunks) {
+                // Q and V of chunk m (their buffers were last read in phase
+                // a): prep waves 3 and 2, whose blocks of T need the least work
+                if (p == 3) {
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) issue_kq(qbase, L::oQ, m, rg);
+                } else if (p == 2) {
+#pragma unroll
+                    for (int sl = 0; sl < 4; ++sl) issue_v(m, sl);
+                }
+                // T of chunk m below the diagonal, column block p:
+                //   Z_i = sum_{p<=k<i} (-A_ik) T_kp,  T_ip = T_ii Z_i,
+                // every product in float32 on the matrix cores.  Then column
+                // block p of -T diag(beta G) and T diag(beta) as two-term
+                // 16-bit expansions, transposed by blocks.
+                const unsigned lF = f_lF();
+                const float *gv = Gv(m);
+                auto ff = [&](unsigned base) { return *reinterpret_cast<const f32x4 *>(smem + base + lF); };
+                auto t3 = [&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    const float bc = gv[kVb * C + 16 * j + x];
+                    const float sw = -bc * gv[kVG * C + 16 * j + x], su = bc;
+                    const unsigned wo = x * 32 + 8 * (qd ^ (2 * (x >> 3)));
+                    // column c = x of block (i, j), scaled by -beta G (for -W)
+                    // and by beta (for U), as two-term 16-bit expansions
+                    auto emit = [&](int i, f32x4 t) {
+                        const unsigned blk = 2 * wy_tidx(i, j) * L::HBLK + wo;
+                        const f32x4 tw = t * sw, tu = t * su;
+                        const X4 twh = cvt4<ET>(tw), tuh = cvt4<ET>(tu);
+                        sts4<ET>(smem, L::oTW + blk, twh);
+                        sts4<ET>(smem, L::oTW + blk + L::HBLK, cvt4<ET>(tw - to_f32x4<ET>(twh)));
+                        sts4<ET>(smem, L::oTU + blk, tuh);
+                        sts4<ET>(smem, L::oTU + blk + L::HBLK, cvt4<ET>(tu - to_f32x4<ET>(tuh)));
+                    };
+                    const f32x4 tjj = ff(L::oTdT + j * L::FBLK);   // T_jj, lane (x, qd): rows 4 qd .., column x
+                    if constexpr (j < NBT - 1) {
+                        // the blocks this column reads, fetched up front; with
+                        // -A stored, Z_i = sum_k (-A_ik) T_kj and T_ij = T_ii Z_i
+                        f32x4 An[NBT][NBT], Td[NBT];
+#pragma unroll
+                        for (int i = j + 1; i < NBT; ++i) {
+                            Td[i] = ff(L::oTd + i * L::FBLK);
+#pragma unroll
+                            for (int k2 = j; k2 < i; ++k2) An[i][k2] = ff(L::oA + wy_aidx(i, k2) * L::FBLK);
+                        }
+                        f32x4 Z[NBT];
+#pragma unroll
+                        for (int i = j + 1; i < NBT; ++i) Z[i] = mma_f32(An[i][j], tjj, zero4());
+                        emit(j, tjj);
+#pragma unroll
+                        for (int i = j + 1; i < NBT; ++i) {
+                            const f32x4 tij = mma_f32(Td[i], Z[i], zero4());
+#pragma unroll
+                            for (int i2 = i + 1; i2 < NBT; ++i2) Z[i2] = mma_f32(An[i2][i], tij, Z[i2]);
+                            emit(i, tij);
+                        }
+                    } else {
+                        emit(j, tjj);
+                    }
+                };
+                switch (p) {
+                case 0: t3(std::integral_constant<int, 0>{}); break;
+                case 1: t3(std::integral_constant<int, 1>{}); break;
+                case 2: t3(std::integral_constant<int, 2>{}); break;
+                default: t3(std::integral_constant<int, 3>{}); break;
+                }
+            }
+            if (p == 3 && n + 2 < nchunks) scan_gates(n + 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+        }
+    }
+}
+
+}  // namespace gdn
