@@ -28,7 +28,9 @@
 //           d_t = beta_t (v_t - g_t S_{t-1} k_t) of the whole chunk (the
 //           ferrox-core page's per-row forward substitution, written for all
 //           rows at once), by blocked forward substitution over 16-token
-//           blocks: D_i = T_ii (RHS_i - sum_{j<i} A_ij D_j)   (MFMA).
+//           blocks: D_i = T_ii (RHS_i - sum_{j<i} A_ij D_j), in float32
+//           throughout (-A, T_ii and the solved blocks float32, float32
+//           matrix-core products, v_mfma_f32_16x16x4_f32).
 //           This is the unit lower triangular system of the metaltile-std
 //           page's steps 4-5.
 //  y_t = (G_t S0 q_t + sum_{j<=t} R[t][j] (q_t.k_j) d_j) / sqrt(Dk)   (MFMA)
@@ -60,17 +62,18 @@ struct ChunkCfg {
     // sixteen different 4-bank groups.
     static constexpr int LDK = DK + EPU;              // sK, sQ
     static constexpr int LDV = DVS + EPU;             // sV
-    static constexpr int LDC = C + EPU;               // sAn, sQKR (16-bit rows of C)
+    static constexpr int LDC = C + EPU;               // sQKR (rows of C input-type elements)
+    static constexpr int LDCF = C + 4;                // sAn (float32 rows of C)
     static constexpr int LDD = 16 + 4;                // sAd (f32 diagonal blocks)
-    static constexpr int LDT = 16 + EPU;              // sTd (diagonal inverses)
+    static constexpr int LDTF = 16 + 4;               // sTd (float32 diagonal inverses)
     static constexpr int oK = 0;
     static constexpr int oQ = oK + C * LDK * ES;
     static constexpr int oV = oQ + C * LDK * ES;
     static constexpr int oAn = oV + C * LDV * ES;
-    static constexpr int oQKR = oAn + C * LDC * ES;
+    static constexpr int oQKR = oAn + C * LDCF * 4;
     static constexpr int oAd = oQKR + C * LDC * ES;
     static constexpr int oTd = oAd + C * LDD * 4;
-    static constexpr int oVec = oTd + C * LDT * ES;   // beta, g, P, Sfx, G, Rlast, block totals
+    static constexpr int oVec = oTd + C * LDTF * 4;   // beta, g, P, Sfx, G, Rlast, block totals
     static constexpr int BYTES = oVec + 7 * C * 4;
     // staging in 16-byte units
     static constexpr int UPK = DK / EPU;
@@ -220,8 +223,8 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     using FR = typename Step<ET>::frag;
     constexpr int BLK = Step<ET>::BLK;
     constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT, NTPW = L::NTPW;
-    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDD = L::LDD,
-                  LDT = L::LDT, EPU = L::EPU;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDCF = L::LDCF, LDD = L::LDD,
+                  LDTF = L::LDTF, EPU = L::EPU;
     constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
     constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
 
@@ -229,10 +232,10 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     ET *sK = reinterpret_cast<ET *>(smem + L::oK);
     ET *sQ = reinterpret_cast<ET *>(smem + L::oQ);
     ET *sV = reinterpret_cast<ET *>(smem + L::oV);
-    ET *sAn = reinterpret_cast<ET *>(smem + L::oAn);    // -A (16-bit)
+    float *sAn = reinterpret_cast<float *>(smem + L::oAn);  // -A (f32)
     ET *sQKR = reinterpret_cast<ET *>(smem + L::oQKR);
     float *sAd = reinterpret_cast<float *>(smem + L::oAd);  // diagonal blocks of A (f32)
-    ET *sTd = reinterpret_cast<ET *>(smem + L::oTd);    // diagonal blocks of (I + A)^-1
+    float *sTd = reinterpret_cast<float *>(smem + L::oTd);  // diagonal blocks of (I + A)^-1 (f32)
     float *sb = reinterpret_cast<float *>(smem + L::oVec);
     float *sg = sb + C;
     float *sP = sg + C;
@@ -481,7 +484,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         float m = pt;
                         for (int bb = jb + 1; bb < tb; ++bb) m *= sBT[bb];
                         const f32x4 R = *reinterpret_cast<const f32x4 *>(sSfx + j0) * m;
-                        st4<ET>(sAn + t * LDC + j0, cvt4<ET>(R * zk * (-bt)));
+                        *reinterpret_cast<f32x4 *>(sAn + t * LDCF + j0) = R * zk * (-bt);
                         st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(R * zq * scale));
                     } else if (jb == tb) {
                         const float *gblk = sg + 16 * tb;
@@ -501,7 +504,7 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             a[r] = (4 * qd + r < x) ? bt * (R[r] * zk[r]) : 0.f;
                             o[r] = (4 * qd + r <= x) ? scale * (R[r] * zq[r]) : 0.f;
                         }
-                        st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
+                        *reinterpret_cast<f32x4 *>(sAn + t * LDCF + j0) = -a;
                         st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
                         *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
                     }
@@ -543,13 +546,16 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;   // A[i][j] = 0 for j >= i
                 }
 #pragma unroll
-                for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
+                for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDTF + c] = s[m];
             }
         }
         lds_barrier();
 
-        // ---- D by blocked forward substitution (per wave, its columns):
-        // RHS = beta (V - G X); D_i = T_ii (RHS_i + sum_{j<i} (-A_ij) D_j).
+        // ---- D by blocked forward substitution (per wave, its columns), in
+        // float32: RHS = beta (V - G X); D_i = T_ii (RHS_i + sum_{j<i} (-A_ij) D_j),
+        // with -A, T_ii and every solved block D_j float32 and every product a
+        // float32 matrix-core product; D is rounded to the input type only
+        // afterwards, as an operand of the output and state products.
         // Fragments over rows t: lane x holds column v, rows 16 i + 4 qd + r.
         f32x4 Da[NBT][NB];
         X4 Df[NBT][NB];
@@ -564,20 +570,15 @@ void chunk_fwd_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 Z[vb] = bv * (vv - gv * Xa[ib][vb]);
             }
 #pragma unroll
-            for (int s = 0; s < NST; ++s) {
-                if (s * BLK >= ib) continue;              // blocks j < ib only
-                FR fa = make_frag<ET>(s, ib, [&](int jb) { return frag_row<ET>(sAn, LDC, 16 * ib, 0, jb, x, qd); });
+            for (int jb = 0; jb < ib; ++jb) {
+                const f32x4 fa = ld4<float>(sAn + (16 * ib + x) * LDCF + 16 * jb + 4 * qd);
 #pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    FR fd = make_frag<ET>(s, ib, [&](int jb) { return Df[jb][vb]; });
-                    Z[vb] = mfma_step(fa, fd, Z[vb]);
-                }
+                for (int vb = 0; vb < NB; ++vb) Z[vb] = mfma_step(fa, Da[jb][vb], Z[vb]);
             }
-            FR ft = make_frag<ET>(0, 1, [&](int) { return frag_row<ET>(sTd, LDT, 16 * ib, 0, 0, x, qd); });
+            const f32x4 ft = ld4<float>(sTd + (16 * ib + x) * LDTF + 4 * qd);
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) {
-                FR fz = make_frag<ET>(0, 1, [&](int) { return cvt4<ET>(Z[vb]); });
-                Da[ib][vb] = mfma_step(ft, fz, zero4());
+                Da[ib][vb] = mfma_step(ft, Z[vb], zero4());
                 Df[ib][vb] = cvt4<ET>(Da[ib][vb]);
             }
         }

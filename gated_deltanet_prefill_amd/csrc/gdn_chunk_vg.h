@@ -144,8 +144,8 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     using FR = typename Step<ET>::frag;
     constexpr int BLK = Step<ET>::BLK;
     constexpr int NBT = L::NBT, NBK = L::NBK, NW = L::NW, NT = L::NT;
-    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDD = L::LDD,
-                  LDT = L::LDT, LDG = L::LDG, EPU = L::EPU;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDCF = L::LDCF, LDD = L::LDD,
+                  LDTF = L::LDTF, LDG = L::LDG, EPU = L::EPU;
     constexpr int NSK = Steps<NBK, BLK>::n;            // contraction steps over Dk
     constexpr int NST = Steps<NBT, BLK>::n;            // contraction steps over C
     constexpr int NPART_V = L::NPART_;
@@ -155,10 +155,10 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     ET *sK = reinterpret_cast<ET *>(smem + L::oK);
     ET *sQ = reinterpret_cast<ET *>(smem + L::oQ);
     ET *sV = reinterpret_cast<ET *>(smem + L::oV);
-    ET *sAn = reinterpret_cast<ET *>(smem + L::oAn);    // -A (16-bit)
+    float *sAn = reinterpret_cast<float *>(smem + L::oAn);  // -A (f32)
     ET *sQKR = reinterpret_cast<ET *>(smem + L::oQKR);
     float *sAd = reinterpret_cast<float *>(smem + L::oAd);  // diagonal blocks of A (f32)
-    ET *sTd = reinterpret_cast<ET *>(smem + L::oTd);    // diagonal blocks of (I + A)^-1
+    float *sTd = reinterpret_cast<float *>(smem + L::oTd);  // diagonal blocks of (I + A)^-1 (f32)
     float *sb = reinterpret_cast<float *>(smem + L::oVec);
     float *sGv = reinterpret_cast<float *>(smem + L::oGv);
     float *sP16 = reinterpret_cast<float *>(smem + L::oP16);
@@ -384,7 +384,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             a *= sb[t];
             o *= scale;
             const int j0 = 16 * bt + 4 * qd;
-            st4<ET>(sAn + t * LDC + j0, cvt4<ET>(-a));
+            *reinterpret_cast<f32x4 *>(sAn + t * LDCF + j0) = -a;
             st4<ET>(sQKR + t * LDC + j0, cvt4<ET>(o));
             *reinterpret_cast<f32x4 *>(sAd + t * LDD + 4 * qd) = a;
         }
@@ -456,7 +456,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
                 const int t = 16 + x;
                 const float bv = sb[t];
-                st4<ET>(sAn + t * LDC + 4 * qd, cvt4<ET>(zk * (-bv)));
+                *reinterpret_cast<f32x4 *>(sAn + t * LDCF + 4 * qd) = zk * (-bv);
                 st4<ET>(sQKR + t * LDC + 4 * qd, cvt4<ET>(zq * scale));
             }
         }
@@ -487,7 +487,7 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     if (4 * m + 3 > j) s[m] -= arow[m][j >> 2][j & 3] * xj;
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDT + c] = from_f32<ET>(s[m]);
+            for (int m = 0; m < 4; ++m) sTd[(base + p + 4 * m) * LDTF + c] = s[m];
         }
 
         // ---- (c) X = (K diag G) S0^T and Y^T = S0 (Q diag G)^T for this wave's columns
@@ -522,7 +522,9 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 
         lds_barrier();                     // the inverses are in LDS
 
-        // ---- (d) D = (I + A)^-1 beta (V - X), blocked forward substitution
+        // ---- (d) D = (I + A)^-1 beta (V - X), blocked forward substitution in
+        // float32 (-A, T_ii and the solved blocks float32, float32 matrix-core
+        // products); D is rounded to the input type only afterwards
         f32x4 Da[NBT][NB];
         X4 Df[NBT][NB];
 #pragma unroll
@@ -535,20 +537,15 @@ void chunk_vg_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 Z[vb] = bv * (vv - Xa[ib][vb]);
             }
 #pragma unroll
-            for (int s = 0; s < NST; ++s) {
-                if (s * BLK >= ib) continue;
-                FR fa = make_frag<ET>(s, ib, [&](int jb) { return frag_row<ET>(sAn, LDC, 16 * ib, 0, jb, x, qd); });
+            for (int jb = 0; jb < ib; ++jb) {
+                const f32x4 fa = ld4<float>(sAn + (16 * ib + x) * LDCF + 16 * jb + 4 * qd);
 #pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    FR fd = make_frag<ET>(s, ib, [&](int jb) { return Df[jb][vb]; });
-                    Z[vb] = mfma_step(fa, fd, Z[vb]);
-                }
+                for (int vb = 0; vb < NB; ++vb) Z[vb] = mfma_step(fa, Da[jb][vb], Z[vb]);
             }
-            FR ft = make_frag<ET>(0, 1, [&](int) { return frag_row<ET>(sTd, LDT, 16 * ib, 0, 0, x, qd); });
+            const f32x4 ft = ld4<float>(sTd + (16 * ib + x) * LDTF + 4 * qd);
 #pragma unroll
             for (int vb = 0; vb < NB; ++vb) {
-                FR fz = make_frag<ET>(0, 1, [&](int) { return cvt4<ET>(Z[vb]); });
-                Da[ib][vb] = mfma_step(ft, fz, zero4());
+                Da[ib][vb] = mfma_step(ft, Z[vb], zero4());
                 Df[ib][vb] = cvt4<ET>(Da[ib][vb]);
             }
         }
