@@ -605,7 +605,6 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // iteration n: phase a builds -W of chunk n and A, T_ii of chunk n+1;
         // phase b the rest of T of chunk n+1 (n = -1 is the pipeline's start)
         for (int n = -1; n < nchunks; ++n) {
-            asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
             const int m = n + 1;
             // ---------------- phase a ----------------
             if (n >= 0) {
