@@ -2,19 +2,23 @@
 // Dk = Dv = 128, chunks of 64 tokens, the chunk's triangular system inverted
 // in float32.
 //
-// Per chunk, in the compact WY form of the metaltile-std gated_delta_wy.rs
-// page (module notes, "Algorithm", steps 4-9: one unit lower triangular
-// solve turns the chunk's keys and values into pseudo-keys and pseudo-values,
-// and the state enters only through products with them), with the decay
-// products of the ferrox-core gdn_chunk.rs page ("The algebra": every ratio
-// of decays is a product of decays):
+// Per chunk, in the per-row form of the ferrox-core gdn_chunk.rs page ("The
+// algebra": unrolled over a chunk, the state enters only through its
+// products with the chunk's keys and queries, the deltas follow from a C x C
+// triangular system, and every ratio of decays is a product of decays):
 //
 //   A[t][j]   = beta_t R[t][j] k_t.k_j  (j < t),   T = (I + A)^-1
-//   W         = T diag(beta G) K,   U = T diag(beta) V            (state free)
+//   M         = K S^T                 the state against the chunk's keys
+//   E         = V - diag(G) M
+//   D         = T diag(beta) E        the true deltas d_t of the chunk
 //   QKR[t][j] = R[t][j] q_t.k_j / sqrt(Dk)  (j <= t)
-//   D         = U - W S^T            the true deltas d_t of the chunk
 //   y         = G (Q S^T) / sqrt(Dk) + QKR D
 //   S        <- G_last S + (diag(Rl) D)^T K,   Rl[t] = R[c-1][t]
+//
+// (I + A) D = diag(beta) E is the same system that the compact WY form of
+// the metaltile-std gated_delta_wy.rs page ("Algorithm", steps 4-9) solves
+// for its pseudo-keys and pseudo-values; here its right-hand side carries the
+// state, so the inverse T is applied once, to E.
 //
 // The triangular system is solved in float32 (the metaltile page's
 // "Numerical precision": float32 is the floor for the solves):
@@ -25,43 +29,42 @@
 //      T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
 //    every product a float32 matrix-core product (v_mfma_f32_16x16x4_f32:
 //    float32 operands, products and accumulation);
-//  * W and U as products of T with the exact 16-bit K and V, T carried as a
-//    two-term expansion T = T_h + T_l (16 significant bits, relative error
-//    <= 2^-17): [T_h | T_l] times [K ; K] is one 16x16x32 MFMA per block.
-//    W is then rounded once to the 16-bit operand of W S^T; U stays float32
-//    and starts the accumulation of D.
+//  * D as the product of T diag(beta), carried as a two-term expansion
+//    T_h + T_l (16 significant bits, relative error <= 2^-17), with E
+//    rounded once to 16 bits: [T_h | T_l] times [E ; E] is one 16x16x32 MFMA
+//    per block.
 //
 // One workgroup of eight waves owns one (batch, value head) slot.  Waves 0-3
 // (state waves) keep the float32 state in registers, 32 value rows each;
-// waves 4-7 (prep waves) build the state-free matrices one chunk ahead and
-// load the inputs.  Each SIMD holds one wave of each kind.  Iteration n has
-// two phases, each closed by a workgroup barrier:
+// waves 4-7 (prep waves) build T one chunk ahead and load the inputs.  Each
+// SIMD holds one wave of each kind.  Iteration n has two phases, each closed
+// by a workgroup barrier:
 //
-//   phase a  state: Y = Q_n S^T, the Q K^T tiles of chunk n -> QKR,
-//                   U_n = T_n diag(beta) V_n (the start of D)
-//            prep:  -W_n = -T_n diag(beta G) K_n; K K^T tiles of chunk n+1
-//                   -> A, the diagonal inverses T_ii;  load K_{n+2}
-//   phase b  state: D = U_n - W_n S^T, y = G Y / sqrt(Dk) + QKR D, state
+//   phase a  state: Y = Q_n S^T and M = K_n S^T from one 16-bit copy of the
+//                   state, the Q K^T tiles of chunk n -> QKR, E = V - G M;
+//                   load K_{n+2}
+//            prep:  the last blocks of T_n below the diagonal; K K^T tiles
+//                   of chunk n+1 -> A, the diagonal inverses T_ii
+//   phase b  state: D = T_n diag(beta) E, y = G Y / sqrt(Dk) + QKR D, state
 //                   update
-//            prep:  the blocks of T_{n+1} below the diagonal and its scaled
-//                   expansions; gate products of chunk n+2; load Q_{n+1},
-//                   V_{n+1}
+//            prep:  the first blocks of T_{n+1} below the diagonal; gate
+//                   products of chunk n+2; load Q_{n+1}, V_{n+1}
 //
-// LDS layouts.  K, Q and -W have 256-byte token rows (keys along the row);
-// the 16-byte unit u of row t sits at u ^ (t % 16).  QKR has 128-byte rows,
-// unit u of row t at u ^ ((t / 2) % 8), and column j = 32 s + 16 h + 4 q + r
-// at position 32 s + 8 q + 4 h + r.  Float32 16x16 blocks (A below the
+// LDS layouts.  K and Q have 256-byte token rows (keys along the row); the
+// 16-byte unit u of row t sits at u ^ (t % 16).  QKR has 128-byte rows, unit
+// u of row t at u ^ ((t / 2) % 8), and column j = 32 s + 16 h + 4 q + r at
+// position 32 s + 8 q + 4 h + r.  Float32 16x16 blocks (A below the
 // diagonal, T_ii by rows and by columns) have 64-byte rows, unit u of row r
-// at u ^ ((r / 4) % 4).  The expansions of T diag(beta G) and T diag(beta)
-// are stored block by block transposed (row c holds column c of the block),
-// 32-byte rows with the 8-byte piece s of row c at s ^ (2 (c / 8)), and read
-// back as row fragments with gfx950's LDS transpose load.
+// at u ^ ((r / 4) % 4).  The expansion of T diag(beta) is stored block by
+// block transposed (row c holds column c of the block), 32-byte rows with
+// the 8-byte piece s of row c at s ^ (2 (c / 8)), and read back as row
+// fragments with gfx950's LDS transpose load.
 //
 // Lane x of value tile vb of state wave w holds value column
 //   32 w + 8 (x/4) + 4 vb + x%4;
 // row 4 qd + r of key tile kb = 2 s + h of the state holds key
 //   32 s + 8 qd + 4 h + r,
-// so that the -W, Q and K row fragments of a 32-key step are single 16-byte
+// so that the K and Q row fragments of a 32-key step are single 16-byte
 // reads of eight consecutive keys.
 #pragma once
 
@@ -79,24 +82,25 @@ struct WyCfg {
     static constexpr int NBK = DK / 16;       // 16-key blocks
     static constexpr int NSK = DK / 32;       // contraction steps over keys
     static constexpr int NB = 2;              // value tiles per state wave
-    static constexpr unsigned KBUF = C * DK * 2;          // one chunk of K, Q or -W
+    static constexpr unsigned KBUF = C * DK * 2;          // one chunk of K or Q
     static constexpr unsigned oK = 0;                     // 3 x K
     static constexpr unsigned oQ = oK + 3 * KBUF;         // Q
     static constexpr unsigned VSL = C * 32 * 2;           // one 32-column V slice
     static constexpr unsigned oV = oQ + KBUF;             // 4 x V slice [C][32]
-    static constexpr unsigned oW = oV + 4 * VSL;          // -W
-    static constexpr unsigned oQKR = oW + KBUF;           // QKR [C][C]
+    static constexpr unsigned oQKR = oV + 4 * VSL;        // QKR [C][C]
     static constexpr unsigned FBLK = 16 * 16 * 4;         // one float32 16x16 block
-    static constexpr unsigned oA = oQKR + C * C * 2;      // -A below the diagonal: 6 blocks
-    static constexpr unsigned oTd = oA + 6 * FBLK;        // T_ii by rows
-    static constexpr unsigned oTdT = oTd + 4 * FBLK;      // T_ii by columns
+    // one chunk's float32 blocks: -A below the diagonal (6), T_ii by rows
+    // (4) and by columns (4); two chunks, by parity
+    static constexpr unsigned ABUF = 14 * FBLK, bTd = 6 * FBLK, bTdT = 10 * FBLK;
+    static constexpr unsigned oA = oQKR + C * C * 2;
     static constexpr unsigned LDD = 20;                   // floats per row of Ad
-    static constexpr unsigned oAd = oTdT + 4 * FBLK;      // A_ii [C][LDD]
+    static constexpr unsigned oAd = oA + 2 * ABUF;        // A_ii [C][LDD]
+    static constexpr unsigned oZ = oAd + C * LDD * 4;     // 2 float32 blocks between the solve's halves
     static constexpr unsigned HBLK = 16 * 16 * 2;         // one 16-bit 16x16 block
-    static constexpr unsigned oTW = oAd + C * LDD * 4;    // -T diag(beta G): 10 blocks x (hi, lo)
-    static constexpr unsigned oTU = oTW + 20 * HBLK;      // T diag(beta): 10 blocks x (hi, lo)
+    static constexpr unsigned TBUF = 20 * HBLK;           // T diag(beta): 10 blocks x (hi, lo)
+    static constexpr unsigned oTU = oZ + 2 * FBLK;        // two chunks, by parity
     static constexpr unsigned NV = 7 * C;                 // floats per gate-vector set
-    static constexpr unsigned oVec = oTU + 20 * HBLK;     // 3 gate-vector sets
+    static constexpr unsigned oVec = oTU + 2 * TBUF;      // 3 gate-vector sets
     static constexpr unsigned oGB = oVec + 3 * NV * 4;    // g, beta of two chunks, as loaded
     static constexpr unsigned BYTES = oGB + 2 * 2 * C * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -137,14 +141,22 @@ __device__ __forceinline__ f32x4 mma_f32(f32x4 a, f32x4 b, f32x4 acc) {
     return acc;
 }
 
-// The C x C tiles of K K^T (prep waves) or Q K^T (state waves) that wave w
-// of a kind computes: tile i has token block ib (rows t of the result) and
-// key block jb (columns j), ib >= jb; tile 0 is the diagonal tile (w, w).
+// The C x C tiles of Q K^T that state wave w computes: tile i has token
+// block ib (rows t of the result) and key block jb (columns j), ib >= jb;
+// tile 0 is the diagonal tile (w, w).
 //   w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
 //   w = 2: (2,2) (3,2)         w = 3: (3,3) (3,0)
 constexpr int wy_ntiles(int w) { return w < 2 ? 3 : 2; }
 constexpr int wy_tile_ib(int w, int i) { return w == 0 ? i : w == 1 ? 1 + i : w == 2 ? 2 + i : 3; }
 constexpr int wy_tile_jb(int w, int i) { return w == 3 ? (i == 0 ? 3 : 0) : w; }
+// The tiles of K K^T that prep wave p computes, tile 0 again the diagonal
+// one; wave 3, which finishes the longest column of T in the same phase,
+// gets no other tile.
+//   p = 0: (0,0) (1,0) (2,0)   p = 1: (1,1) (2,1) (3,1)
+//   p = 2: (2,2) (3,2) (3,0)   p = 3: (3,3)
+constexpr int kk_ntiles(int p) { return p == 3 ? 1 : 3; }
+constexpr int kk_tile_ib(int p, int i) { return p < 2 ? p + i : p == 2 ? (i == 0 ? 2 : 3) : 3; }
+constexpr int kk_tile_jb(int p, int i) { return p < 2 ? p : p == 2 ? (i == 2 ? 0 : 2) : 3; }
 // index of block (i, j), i > j, among the six blocks below the diagonal
 constexpr int wy_aidx(int i, int j) { return i * (i - 1) / 2 + j; }
 // index of block (i, j), i >= j, among the ten blocks of the lower triangle
@@ -191,13 +203,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const int nchunks = (T + C - 1) / C;
 
     // ---- lane-dependent LDS byte offsets
-    // K/Q/-W row fragment (16 bytes at unit 4 s + qd of row 16 b + x): ^ 64 s, + 4096 b
+    // K/Q row fragment (16 bytes at unit 4 s + qd of row 16 b + x): ^ 64 s, + 4096 b
     auto f_lKt = [&]() { return (unsigned)(x * 256 + (((qd ^ x) & 15) << 4)); };
-    // K transpose read, rows 16 jb + 4 qd + x/4, keys 16 kt + 4 (x%4) ..: ^ 32 kt, + 4096 jb
-    auto f_lKtr = [&]() {
-        const int r4 = 4 * qd + (x >> 2);
-        return (unsigned)(r4 * 256 + (((((x >> 1) & 1) ^ r4) & 15) << 4) + ((x & 1) << 3));
-    };
     // K transpose read for the state update, rows r0 + r4, keys 32 s + 4 h +
     // 8 (x%4) .. +3 (lane x then receives key 32 s + 4 h + 8 (x/4) + x%4):
     // ^ 64 s, + 8 h, + 256 r0
@@ -205,8 +212,6 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int r4 = 4 * qd + (x >> 2);
         return (unsigned)(r4 * 256 + ((((x & 3) ^ r4) & 15) << 4));
     };
-    // -W write: token 16 ib + x, keys 16 kt + 4 qd .. + 3: ^ 32 kt, + 4096 ib
-    auto f_lWp = [&]() { return (unsigned)(x * 256 + ((((qd >> 1) ^ x) & 15) << 4) + 8 * (qd & 1)); };
     // QKR rows 16 tb + x, the 4 columns 16 jb + 4 qd ..: (this ^ 64 (jb/2)) +
     // 8 (jb%2) + 2048 tb; the 8 columns of blocks 2 s, 2 s + 1: ^ 64 s
     auto f_lA = [&]() { return (unsigned)(x * 128 + (((qd ^ (x >> 1)) & 7) << 4)); };
@@ -219,18 +224,18 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // row-x entries of columns 4 qd .. 4 qd + 3
     auto f_lT = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 32 + 8 * ((x & 3) ^ ((qd >> 1) << 1))); };
 
-    // ---------------- input loads (prep waves) ----------------
+    // ---------------- input loads ----------------
     // Chunks of K, Q and V go from global memory straight into LDS
     // (global_load_lds_dwordx4: lane l of the wave writes the 16 bytes at
     // 16 l of a 1 KB block), written as inline assembly so that the compiler
     // does not wait for the transfer before the wave's next LDS access; the
-    // prep waves, which issue no other global memory operations, await them
-    // with s_waitcnt vmcnt(0) before the barrier that closes phase b.  Prep
-    // wave p fills K/Q rows 16 p .. 16 p + 15 and the V columns 32 p .. 32 p
-    // + 31.  The swizzle of K and Q is applied on the source side.  Rows past
-    // the end of the sequence fetch the last row again; with g = 1 and
-    // beta = 0 there, those rows add nothing (A, W, U and D vanish on them,
-    // and their y rows are not stored).
+    // issuing waves await them with s_waitcnt vmcnt(0) before the barrier
+    // that closes the phase.  State wave w fills K rows 16 w .. 16 w + 15,
+    // prep wave 3 all of Q and prep wave 2 all of V.  The swizzle of K and Q
+    // is applied on the source side.  Rows past the end of the sequence fetch
+    // the last row again; with g = 1 and beta = 0 there, those rows add
+    // nothing (their rows of A and columns of T diag(beta) vanish, so D is
+    // zero on them, and their y rows are not stored).
     const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * DV;
     const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
     const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
@@ -410,22 +415,27 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         issue_inputs(-1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                           // A, T_ii of chunk 0
-        lds_barrier();                           // T of chunk 0, Q_0, V_0
+        lds_barrier();                           // first blocks of T of chunk 0, Q_0, V_0
         for (int n = 0; n < nchunks; ++n) {
             asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
             issue_inputs(n);
             const unsigned lKt = f_lKt(), lA = f_lA();
             const unsigned kbn = L::oK + (n % 3) * L::KBUF;
             const float *gv = Gv(n);
-            f32x4 D[NBT][NB], Y[NB][NBT];
+            f32x4 Y[NB][NBT];
+            X4 E[NBT][NB], Vf[NBT][NB];
             // ---------------- phase a ----------------
             {
-                // Y^T = S Q^T, and this wave's Q K^T tiles from the same Q fragments
+                // Y^T = S Q^T and M = K S^T from the same 16-bit fragments of
+                // the state, and this wave's Q K^T tiles from the same Q and K
+                // fragments.  M: lane (x, qd) of tile (tb, vb) holds tokens
+                // 16 tb + 4 qd .. + 3 of value column vcol(vb, x).
+                f32x4 M[NBT][NB];
 #pragma unroll
                 for (int tb = 0; tb < NBT; ++tb)
 #pragma unroll
-                    for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = zero4();
-                auto qk_tiles = [&](auto W) {
+                    for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = M[tb][vb] = zero4();
+                auto products = [&](auto W) {
                     constexpr int wc = decltype(W)::value;
                     constexpr int nt = wy_ntiles(wc);
                     f32x4 acc[nt];
@@ -438,18 +448,25 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                         for (int vb = 0; vb < NB; ++vb)
                             fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
-                        X8 fq[NBT];
+                        X8 fq[NBT], fk[NBT];
 #pragma unroll
-                        for (int tb = 0; tb < NBT; ++tb) fq[tb] = lds8<ET>(smem, L::oQ + lo + 4096 * tb);
+                        for (int tb = 0; tb < NBT; ++tb) {
+                            fq[tb] = lds8<ET>(smem, L::oQ + lo + 4096 * tb);
+                            fk[tb] = lds8<ET>(smem, kbn + lo + 4096 * tb);
+                        }
 #pragma unroll
                         for (int tb = 0; tb < NBT; ++tb)
 #pragma unroll
-                            for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = mfma(fs[vb], fq[tb], Y[vb][tb]);
+                            for (int vb = 0; vb < NB; ++vb) {
+                                Y[vb][tb] = mfma(fs[vb], fq[tb], Y[vb][tb]);
+                                M[tb][vb] = mfma(fk[tb], fs[vb], M[tb][vb]);
+                            }
 #pragma unroll
-                        for (int i = 0; i < nt; ++i) {
-                            const X8 fk = lds8<ET>(smem, kbn + lo + 4096 * wy_tile_jb(wc, i));
-                            acc[i] = mfma(fk, fq[wy_tile_ib(wc, i)], acc[i]);
-                        }
+                        for (int i = 0; i < nt; ++i)
+                            acc[i] = mfma(fk[wy_tile_jb(wc, i)], fq[wy_tile_ib(wc, i)], acc[i]);
+                        // one key step at a time: the 16-bit copy of the
+                        // state is formed step by step, not held whole
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                     // QKR = R (Q K^T) / sqrt(Dk), lower including the diagonal
                     {
@@ -467,59 +484,46 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
                 };
                 switch (w) {
-                case 0: qk_tiles(std::integral_constant<int, 0>{}); break;
-                case 1: qk_tiles(std::integral_constant<int, 1>{}); break;
-                case 2: qk_tiles(std::integral_constant<int, 2>{}); break;
-                default: qk_tiles(std::integral_constant<int, 3>{}); break;
+                case 0: products(std::integral_constant<int, 0>{}); break;
+                case 1: products(std::integral_constant<int, 1>{}); break;
+                case 2: products(std::integral_constant<int, 2>{}); break;
+                default: products(std::integral_constant<int, 3>{}); break;
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            {
-                // U = T diag(beta) V for this wave's value columns: the
-                // start of D.  [T_h | T_l] [V ; V] per block, V read with the
-                // permuted columns of the value tiles.
-                const unsigned vsl = L::oV + w * L::VSL + f_lVs(), lT = f_lT();
-                X4 vc[NBT][NB];
-#pragma unroll
-                for (int jb = 0; jb < NBT; ++jb)
-#pragma unroll
-                    for (int vb = 0; vb < NB; ++vb) vc[jb][vb] = ld_tr<ET>(smem, vsl + 8 * vb + 1024 * jb);
+                // the right-hand side E = V - G M in two 16-bit parts: V as
+                // loaded (exact) and -G M rounded once; V read with the
+                // permuted columns of the value tiles
+                const unsigned vsl = L::oV + w * L::VSL + f_lVs();
 #pragma unroll
                 for (int tb = 0; tb < NBT; ++tb) {
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gv + kVG * C + 16 * tb + 4 * qd);
 #pragma unroll
-                    for (int vb = 0; vb < NB; ++vb) D[tb][vb] = zero4();
-#pragma unroll
-                    for (int jb = 0; jb <= tb; ++jb) {
-                        const unsigned to = L::oTU + 2 * wy_tidx(tb, jb) * L::HBLK + lT;
-                        const X8 ft = cat8<ET>(ld_tr<ET>(smem, to), ld_tr<ET>(smem, to + L::HBLK));
-#pragma unroll
-                        for (int vb = 0; vb < NB; ++vb)
-                            D[tb][vb] = mfma(ft, cat8<ET>(vc[jb][vb], vc[jb][vb]), D[tb][vb]);
+                    for (int vb = 0; vb < NB; ++vb) {
+                        Vf[tb][vb] = ld_tr<ET>(smem, vsl + 8 * vb + 1024 * tb);
+                        E[tb][vb] = cvt4<ET>(g4 * M[tb][vb] * -1.f);
                     }
                 }
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
             // ---------------- phase b ----------------
-            // The state's 16-bit operands are formed again here rather than
-            // kept from phase a (32 registers fewer across the barrier).
-#pragma unroll
-            for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) asm volatile("" : "+v"(S[kb][vb]));
             {
-                // D = U + (-W) S^T
+                // D = T diag(beta) V + T diag(beta) (-G M): [T_h | T_l] [V ; V]
+                // and [T_h | T_l] [-G M ; -G M] per block
+                const unsigned tub = L::oTU + (n & 1) * L::TBUF + f_lT();
+                f32x4 D[NBT][NB];
 #pragma unroll
-                for (int s = 0; s < NSK; ++s) {
-                    X8 fs[NB];
+                for (int tb = 0; tb < NBT; ++tb) {
 #pragma unroll
-                    for (int vb = 0; vb < NB; ++vb)
-                        fs[vb] = cat8<ET>(cvt4<ET>(S[2 * s][vb]), cvt4<ET>(S[2 * s + 1][vb]));
+                    for (int vb = 0; vb < NB; ++vb) D[tb][vb] = zero4();
 #pragma unroll
-                    for (int tb = 0; tb < NBT; ++tb) {
-                        const X8 fw = lds8<ET>(smem, L::oW + (lKt ^ (64 * s)) + 4096 * tb);
+                    for (int jb = 0; jb <= tb; ++jb) {
+                        const unsigned to = tub + 2 * wy_tidx(tb, jb) * L::HBLK;
+                        const X8 ft = cat8<ET>(ld_tr<ET>(smem, to), ld_tr<ET>(smem, to + L::HBLK));
 #pragma unroll
-                        for (int vb = 0; vb < NB; ++vb) D[tb][vb] = mfma(fw, fs[vb], D[tb][vb]);
+                        for (int vb = 0; vb < NB; ++vb) {
+                            D[tb][vb] = mfma(ft, cat8<ET>(Vf[jb][vb], Vf[jb][vb]), D[tb][vb]);
+                            D[tb][vb] = mfma(ft, cat8<ET>(E[jb][vb], E[jb][vb]), D[tb][vb]);
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -602,55 +606,53 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // ================= prep waves =================
         const int p = w;
         lds_barrier();
-        // iteration n: phase a builds -W of chunk n and A, T_ii of chunk n+1;
-        // phase b the rest of T of chunk n+1 (n = -1 is the pipeline's start)
+        // Block (i, j) of T diag(beta) of chunk c, given in float32 (lane
+        // (x, qd): rows 4 qd .. + 3, column x): scaled by beta of column x
+        // and stored as a two-term 16-bit expansion, transposed by blocks.
+        auto emit = [&](int c, int i, int j, f32x4 t) {
+            const float bc = Gv(c)[kVb * C + 16 * j + x];
+            const unsigned blk = L::oTU + (c & 1) * L::TBUF + 2 * wy_tidx(i, j) * L::HBLK +
+                                 x * 32 + 8 * (qd ^ (2 * (x >> 3)));
+            const f32x4 tu = t * bc;
+            const X4 h = cvt4<ET>(tu);
+            sts4<ET>(smem, blk, h);
+            sts4<ET>(smem, blk + L::HBLK, cvt4<ET>(tu - to_f32x4<ET>(h)));
+        };
+        // Partial sums Z_2, Z_3 of column 0, carried from the first half of
+        // the solve (wave 0) to its second half (wave 3) in 16-byte slots
+        // indexed by lane
+        auto zst = [&](int i, f32x4 v) { *reinterpret_cast<f32x4 *>(smem + L::oZ + i * L::FBLK + 16 * lane) = v; };
+        auto zld = [&](int i) { return *reinterpret_cast<const f32x4 *>(smem + L::oZ + i * L::FBLK + 16 * lane); };
+        // iteration n: phase a finishes T of chunk n and builds A, T_ii of
+        // chunk n+1; phase b starts T of chunk n+1 (n = -1 is the pipeline's
+        // start).  The blocks below the diagonal, with -A stored:
+        //   Z_i = sum_{j<=k<i} (-A_ik) T_kj,  T_ij = T_ii Z_i,
+        // every product in float32 on the matrix cores.  First half (phase
+        // b, wave p = column p): column 0 up to T_10 and the terms of Z_2,
+        // Z_3 through T_10; columns 1 and 2 whole.  Second half (phase a of
+        // the next iteration, wave 3): T_20, T_30.
         for (int n = -1; n < nchunks; ++n) {
             const int m = n + 1;
+            const unsigned lF = f_lF();
+            auto ff = [&](unsigned base) { return *reinterpret_cast<const f32x4 *>(smem + base + lF); };
             // ---------------- phase a ----------------
-            if (n >= 0) {
-                // -W^T = K^T (-T diag(beta G))^T for key tiles 2 p, 2 p + 1:
-                // lane (x, qd) of tile (kt, ib) holds keys 16 kt + 4 qd .. + 3
-                // of token 16 ib + x, one 8-byte write into the token rows of -W.
-                const unsigned kbn = L::oK + (n % 3) * L::KBUF;
-                const unsigned lKtr = f_lKtr(), lT = f_lT(), lWp = f_lWp();
-                X4 kc[NBT][2];
-#pragma unroll
-                for (int jb = 0; jb < NBT; ++jb)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) kc[jb][c] = ld_tr<ET>(smem, kbn + (lKtr ^ (32 * (2 * p + c))) + 4096 * jb);
-                X8 ft[NBT * (NBT + 1) / 2];
-#pragma unroll
-                for (int ib = 0; ib < NBT; ++ib)
-#pragma unroll
-                    for (int jb = 0; jb <= ib; ++jb) {
-                        const unsigned to = L::oTW + 2 * wy_tidx(ib, jb) * L::HBLK + lT;
-                        ft[wy_tidx(ib, jb)] = cat8<ET>(ld_tr<ET>(smem, to), ld_tr<ET>(smem, to + L::HBLK));
-                    }
-                f32x4 acc[NBT][2];
-#pragma unroll
-                for (int ib = 0; ib < NBT; ++ib)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        acc[ib][c] = zero4();
-#pragma unroll
-                        for (int jb = 0; jb <= ib; ++jb)
-                            acc[ib][c] = mfma(cat8<ET>(kc[jb][c], kc[jb][c]), ft[wy_tidx(ib, jb)], acc[ib][c]);
-                    }
-#pragma unroll
-                for (int ib = 0; ib < NBT; ++ib)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        sts4<ET>(smem, L::oW + (lWp ^ (32 * (2 * p + c))) + 4096 * ib, cvt4<ET>(acc[ib][c]));
+            if (n >= 0 && p == 3) {
+                const unsigned ab = L::oA + (n & 1) * L::ABUF;
+                const f32x4 t20 = mma_f32(ff(ab + L::bTd + 2 * L::FBLK), zld(0), zero4());
+                const f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 2) * L::FBLK), t20, zld(1));
+                emit(n, 2, 0, t20);
+                emit(n, 3, 0, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
             }
             if (m < nchunks) {
                 // K K^T tiles of chunk m -> A (float32): the diagonal tile to
                 // Ad (for the inverse), the tiles below it to their blocks
                 const unsigned kbm = L::oK + (m % 3) * L::KBUF;
-                const unsigned lKt = f_lKt(), lF = f_lF();
+                const unsigned ab = L::oA + (m & 1) * L::ABUF;
+                const unsigned lKt = f_lKt();
                 const float *gv = Gv(m);
                 auto kk_tiles = [&](auto W) {
                     constexpr int wc = decltype(W)::value;
-                    constexpr int nt = wy_ntiles(wc);
+                    constexpr int nt = kk_ntiles(wc);
                     f32x4 acc[nt];
 #pragma unroll
                     for (int i = 0; i < nt; ++i) acc[i] = zero4();
@@ -659,8 +661,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         const unsigned lo = lKt ^ (64 * s);
 #pragma unroll
                         for (int i = 0; i < nt; ++i)
-                            acc[i] = mfma(lds8<ET>(smem, kbm + lo + 4096 * wy_tile_jb(wc, i)),
-                                          lds8<ET>(smem, kbm + lo + 4096 * wy_tile_ib(wc, i)), acc[i]);
+                            acc[i] = mfma(lds8<ET>(smem, kbm + lo + 4096 * kk_tile_jb(wc, i)),
+                                          lds8<ET>(smem, kbm + lo + 4096 * kk_tile_ib(wc, i)), acc[i]);
                     }
                     {
                         const int t = 16 * wc + x;
@@ -673,10 +675,10 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
 #pragma unroll
                     for (int i = 1; i < nt; ++i) {
-                        const int ib = wy_tile_ib(wc, i), jb = wy_tile_jb(wc, i);
+                        const int ib = kk_tile_ib(wc, i), jb = kk_tile_jb(wc, i);
                         const f32x4 R = off_ratio(gv, ib, jb);
                         const float bt = gv[kVb * C + 16 * ib + x];
-                        *reinterpret_cast<f32x4 *>(smem + L::oA + wy_aidx(ib, jb) * L::FBLK + lF) = R * acc[i] * (-bt);
+                        *reinterpret_cast<f32x4 *>(smem + ab + wy_aidx(ib, jb) * L::FBLK + lF) = R * acc[i] * (-bt);
                     }
                 };
                 switch (p) {
@@ -720,8 +722,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
                     // rows r = pt + 4 mm of column c, into the block by rows
                     // and the block by columns
-                    float *td = reinterpret_cast<float *>(smem + L::oTd + p * L::FBLK);
-                    float *tdt = reinterpret_cast<float *>(smem + L::oTdT + p * L::FBLK);
+                    float *td = reinterpret_cast<float *>(smem + ab + L::bTd + p * L::FBLK);
+                    float *tdt = reinterpret_cast<float *>(smem + ab + L::bTdT + p * L::FBLK);
 #pragma unroll
                     for (int mm = 0; mm < 4; ++mm) {
                         const int r = pt + 4 * mm;
@@ -742,61 +744,29 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                     for (int sl = 0; sl < 4; ++sl) issue_v(m, sl);
                 }
-                // T of chunk m below the diagonal, column block p:
-                //   Z_i = sum_{p<=k<i} (-A_ik) T_kp,  T_ip = T_ii Z_i,
-                // every product in float32 on the matrix cores.  Then column
-                // block p of -T diag(beta G) and T diag(beta) as two-term
-                // 16-bit expansions, transposed by blocks.
-                const unsigned lF = f_lF();
-                const float *gv = Gv(m);
-                auto ff = [&](unsigned base) { return *reinterpret_cast<const f32x4 *>(smem + base + lF); };
-                auto t3 = [&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    const float bc = gv[kVb * C + 16 * j + x];
-                    const float sw = -bc * gv[kVG * C + 16 * j + x], su = bc;
-                    const unsigned wo = x * 32 + 8 * (qd ^ (2 * (x >> 3)));
-                    // column c = x of block (i, j), scaled by -beta G (for -W)
-                    // and by beta (for U), as two-term 16-bit expansions
-                    auto emit = [&](int i, f32x4 t) {
-                        const unsigned blk = 2 * wy_tidx(i, j) * L::HBLK + wo;
-                        const f32x4 tw = t * sw, tu = t * su;
-                        const X4 twh = cvt4<ET>(tw), tuh = cvt4<ET>(tu);
-                        sts4<ET>(smem, L::oTW + blk, twh);
-                        sts4<ET>(smem, L::oTW + blk + L::HBLK, cvt4<ET>(tw - to_f32x4<ET>(twh)));
-                        sts4<ET>(smem, L::oTU + blk, tuh);
-                        sts4<ET>(smem, L::oTU + blk + L::HBLK, cvt4<ET>(tu - to_f32x4<ET>(tuh)));
-                    };
-                    const f32x4 tjj = ff(L::oTdT + j * L::FBLK);   // T_jj, lane (x, qd): rows 4 qd .., column x
-                    if constexpr (j < NBT - 1) {
-                        // the blocks this column reads, fetched up front; with
-                        // -A stored, Z_i = sum_k (-A_ik) T_kj and T_ij = T_ii Z_i
-                        f32x4 An[NBT][NBT], Td[NBT];
-#pragma unroll
-                        for (int i = j + 1; i < NBT; ++i) {
-                            Td[i] = ff(L::oTd + i * L::FBLK);
-#pragma unroll
-                            for (int k2 = j; k2 < i; ++k2) An[i][k2] = ff(L::oA + wy_aidx(i, k2) * L::FBLK);
-                        }
-                        f32x4 Z[NBT];
-#pragma unroll
-                        for (int i = j + 1; i < NBT; ++i) Z[i] = mma_f32(An[i][j], tjj, zero4());
-                        emit(j, tjj);
-#pragma unroll
-                        for (int i = j + 1; i < NBT; ++i) {
-                            const f32x4 tij = mma_f32(Td[i], Z[i], zero4());
-#pragma unroll
-                            for (int i2 = i + 1; i2 < NBT; ++i2) Z[i2] = mma_f32(An[i2][i], tij, Z[i2]);
-                            emit(i, tij);
-                        }
-                    } else {
-                        emit(j, tjj);
-                    }
-                };
-                switch (p) {
-                case 0: t3(std::integral_constant<int, 0>{}); break;
-                case 1: t3(std::integral_constant<int, 1>{}); break;
-                case 2: t3(std::integral_constant<int, 2>{}); break;
-                default: t3(std::integral_constant<int, 3>{}); break;
+                const unsigned ab = L::oA + (m & 1) * L::ABUF;
+                const f32x4 tpp = ff(ab + L::bTdT + p * L::FBLK);   // T_pp, lane (x, qd): rows 4 qd .., column x
+                emit(m, p, p, tpp);
+                if (p == 0) {
+                    const f32x4 z1 = mma_f32(ff(ab + wy_aidx(1, 0) * L::FBLK), tpp, zero4());
+                    f32x4 z2 = mma_f32(ff(ab + wy_aidx(2, 0) * L::FBLK), tpp, zero4());
+                    f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 0) * L::FBLK), tpp, zero4());
+                    const f32x4 t10 = mma_f32(ff(ab + L::bTd + 1 * L::FBLK), z1, zero4());
+                    z2 = mma_f32(ff(ab + wy_aidx(2, 1) * L::FBLK), t10, z2);
+                    z3 = mma_f32(ff(ab + wy_aidx(3, 1) * L::FBLK), t10, z3);
+                    zst(0, z2);
+                    zst(1, z3);
+                    emit(m, 1, 0, t10);
+                } else if (p == 1) {
+                    const f32x4 z2 = mma_f32(ff(ab + wy_aidx(2, 1) * L::FBLK), tpp, zero4());
+                    f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 1) * L::FBLK), tpp, zero4());
+                    const f32x4 t21 = mma_f32(ff(ab + L::bTd + 2 * L::FBLK), z2, zero4());
+                    z3 = mma_f32(ff(ab + wy_aidx(3, 2) * L::FBLK), t21, z3);
+                    emit(m, 2, 1, t21);
+                    emit(m, 3, 1, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
+                } else if (p == 2) {
+                    const f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 2) * L::FBLK), tpp, zero4());
+                    emit(m, 3, 2, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
                 }
             }
             if (p == 3 && n + 2 < nchunks) scan_gates(n + 2);
