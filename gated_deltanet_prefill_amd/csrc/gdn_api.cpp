@@ -87,17 +87,18 @@ bool seq_for(int dtype, int T) { return T <= (dtype == GDN_F32 ? 12 : 6); }
 // dtypes.  16 keeps the most work in flight per token and wins on grids of
 // many (batch, head) slots and on short sequences; 32 wins from 32 tokens on
 // grids of up to 256 slots (the generic kernel then runs several value
-// slices per slot); the pipelined 64-token kernel (16-bit inputs,
-// 128-dimensional heads) wins once each slot has enough chunks to fill its
-// pipeline, which takes more tokens the more slots share the chip.  float32
-// inputs run their products at the f32 MFMA rate: 16 for 128-dimensional
-// heads, 32 from 32 tokens for smaller ones.
+// slices per slot).  For 16-bit inputs with 128-dimensional heads the
+// pipelined 64-token kernel wins from 48 tokens on up to 64 slots (where it
+// runs four workgroups per slot) and on 129..256 slots, and from 128 tokens
+// on other grids.  float32 inputs run their products at the f32 MFMA rate:
+// 16 for 128-dimensional heads, 32 from 32 tokens for smaller ones.
 int chunk_for(int dtype, int Dk, int Dv, long slots, int T) {
     if (dtype == GDN_F32) return (Dk <= 64 && Dv <= 64 && T >= 32) ? 32 : 16;
     if (Dk == 128 && Dv == 128) {
-        if (16L * T >= 3L * slots && (T >= 96 || (T >= 48 && slots > 256))) return 64;
-        if (T >= 32 && slots <= 256) return 32;
-        return 16;
+        if (T < 32) return 16;
+        if (slots <= 64 || (slots > 128 && slots <= 256)) return T < 48 ? 32 : 64;
+        if (slots <= 128) return T < 128 ? 32 : 64;
+        return T < 128 ? 16 : 64;
     }
     return (T >= 64 || (T >= 32 && slots <= 256)) ? 32 : 16;
 }

@@ -74,20 +74,26 @@
 
 namespace gdn {
 
-template <typename ET>
+template <typename ET, int NSW_>
 struct WyCfg {
     static_assert(sizeof(ET) == 2, "16-bit element types only");
+    static_assert(NSW_ == 4 || NSW_ == 2, "four or two state waves");
     static constexpr int C = 64, DK = 128, DV = 128;
+    static constexpr int NSW = NSW_;          // state waves
+    static constexpr int NP = 8 - NSW;        // prep waves
+    static constexpr int NB = NSW == 4 ? 2 : 1;           // value tiles per state wave
+    static constexpr int ROWS = 16 * NB * NSW;            // value rows per workgroup
+    static constexpr int NSPLIT = DV / ROWS;              // workgroups per slot
     static constexpr int NBT = C / 16;        // 16-token blocks
     static constexpr int NBK = DK / 16;       // 16-key blocks
     static constexpr int NSK = DK / 32;       // contraction steps over keys
-    static constexpr int NB = 2;              // value tiles per state wave
     static constexpr unsigned KBUF = C * DK * 2;          // one chunk of K or Q
     static constexpr unsigned oK = 0;                     // 3 x K
     static constexpr unsigned oQ = oK + 3 * KBUF;         // Q
-    static constexpr unsigned VSL = C * 32 * 2;           // one 32-column V slice
-    static constexpr unsigned oV = oQ + KBUF;             // 4 x V slice [C][32]
-    static constexpr unsigned oQKR = oV + 4 * VSL;        // QKR [C][C]
+    static constexpr unsigned VRB = 32 * NB;              // bytes per token row of a V slice
+    static constexpr unsigned VSL = C * VRB;              // one state wave's V slice
+    static constexpr unsigned oV = oQ + KBUF;             // NSW x V slice [C][16 NB]
+    static constexpr unsigned oQKR = oV + NSW * VSL;      // QKR [C][C]
     static constexpr unsigned FBLK = 16 * 16 * 4;         // one float32 16x16 block
     // one chunk's float32 blocks: -A below the diagonal (6), T_ii by rows
     // (4) and by columns (4); two chunks, by parity
@@ -141,28 +147,69 @@ __device__ __forceinline__ f32x4 mma_f32(f32x4 a, f32x4 b, f32x4 acc) {
     return acc;
 }
 
-// The C x C tiles of Q K^T that state wave w computes: tile i has token
-// block ib (rows t of the result) and key block jb (columns j), ib >= jb;
-// tile 0 is the diagonal tile (w, w).
-//   w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
-//   w = 2: (2,2) (3,2)         w = 3: (3,3) (3,0)
-constexpr int wy_ntiles(int w) { return w < 2 ? 3 : 2; }
-constexpr int wy_tile_ib(int w, int i) { return w == 0 ? i : w == 1 ? 1 + i : w == 2 ? 2 + i : 3; }
-constexpr int wy_tile_jb(int w, int i) { return w == 3 ? (i == 0 ? 3 : 0) : w; }
-// The tiles of K K^T that prep wave p computes, tile 0 again the diagonal
-// one; wave 3, which finishes the longest column of T in the same phase,
-// gets no other tile.
-//   p = 0: (0,0) (1,0) (2,0)   p = 1: (1,1) (2,1) (3,1)
-//   p = 2: (2,2) (3,2) (3,0)   p = 3: (3,3)
-constexpr int kk_ntiles(int p) { return p == 3 ? 1 : 3; }
-constexpr int kk_tile_ib(int p, int i) { return p < 2 ? p + i : p == 2 ? (i == 0 ? 2 : 3) : 3; }
-constexpr int kk_tile_jb(int p, int i) { return p < 2 ? p : p == 2 ? (i == 2 ? 0 : 2) : 3; }
+// Which wave computes which C x C tile of Q K^T and K K^T.  Tile (ib, jb)
+// has token block ib (rows t of the result) and key block jb (columns j),
+// ib >= jb.  Prep waves 0-3 hold the diagonal K K^T tile (p, p), whose
+// inverse they form.  With four state and four prep waves:
+//   Q K^T, state wave w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
+//                         w = 2: (2,2) (3,2)         w = 3: (3,3) (3,0)
+//   K K^T, prep wave  p = 0: (0,0) (1,0) (2,0)   p = 1: (1,1) (2,1) (3,1)
+//                         p = 2: (2,2) (3,2) (3,0)   p = 3: (3,3)
+// (prep wave 3 finishes the longest column of T in the same phase).  With
+// two state and six prep waves:
+//   Q K^T, state wave w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
+//          prep wave  p = 0: (2,2) (3,2)         p = 1: (3,3) (3,0)
+//   K K^T, prep wave  p = 0: (0,0)   p = 1: (1,1)   p = 2: (2,2) (1,0) (2,0)
+//                     p = 3: (3,3) (3,0) (2,1)   p = 4: (3,1) (3,2)
+// (prep wave 4 finishes the longest column of T, prep wave 5 loads K).
+struct Tile { int ib, jb; };
+template <int N> struct Tiles { static constexpr int n = N; Tile t[N > 0 ? N : 1]; };
+template <int NSW> constexpr auto qk_state(int w) {
+    if (NSW == 4) {
+        switch (w) {
+        case 0: return Tiles<3>{{{0, 0}, {1, 0}, {2, 0}}};
+        case 1: return Tiles<3>{{{1, 1}, {2, 1}, {3, 1}}};
+        case 2: return Tiles<3>{{{2, 2}, {3, 2}, {-1, -1}}};
+        default: return Tiles<3>{{{3, 3}, {3, 0}, {-1, -1}}};
+        }
+    }
+    return w == 0 ? Tiles<3>{{{0, 0}, {1, 0}, {2, 0}}} : Tiles<3>{{{1, 1}, {2, 1}, {3, 1}}};
+}
+template <int NSW> constexpr auto qk_prep(int p) {
+    if (NSW == 2 && p == 0) return Tiles<2>{{{2, 2}, {3, 2}}};
+    if (NSW == 2 && p == 1) return Tiles<2>{{{3, 3}, {3, 0}}};
+    return Tiles<2>{{{-1, -1}, {-1, -1}}};
+}
+template <int NSW> constexpr auto kk_prep(int p) {
+    if (NSW == 4) {
+        switch (p) {
+        case 0: return Tiles<3>{{{0, 0}, {1, 0}, {2, 0}}};
+        case 1: return Tiles<3>{{{1, 1}, {2, 1}, {3, 1}}};
+        case 2: return Tiles<3>{{{2, 2}, {3, 2}, {3, 0}}};
+        default: return Tiles<3>{{{3, 3}, {-1, -1}, {-1, -1}}};
+        }
+    }
+    switch (p) {
+    case 0: return Tiles<3>{{{0, 0}, {-1, -1}, {-1, -1}}};
+    case 1: return Tiles<3>{{{1, 1}, {-1, -1}, {-1, -1}}};
+    case 2: return Tiles<3>{{{2, 2}, {1, 0}, {2, 0}}};
+    case 3: return Tiles<3>{{{3, 3}, {3, 0}, {2, 1}}};
+    case 4: return Tiles<3>{{{3, 1}, {3, 2}, {-1, -1}}};
+    default: return Tiles<3>{{{-1, -1}, {-1, -1}, {-1, -1}}};
+    }
+}
+// number of real tiles (ib >= 0) in a list
+template <typename TL> constexpr int ntiles(TL tl) {
+    int c = 0;
+    for (int i = 0; i < TL::n; ++i) c += tl.t[i].ib >= 0;
+    return c;
+}
 // index of block (i, j), i > j, among the six blocks below the diagonal
 constexpr int wy_aidx(int i, int j) { return i * (i - 1) / 2 + j; }
 // index of block (i, j), i >= j, among the ten blocks of the lower triangle
 constexpr int wy_tidx(int i, int j) { return i * (i + 1) / 2 + j; }
 
-template <typename ET>
+template <typename ET, int NSW>
 __global__ __launch_bounds__(512, 1)
 void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                      const ET *__restrict__ v, const float *__restrict__ g,
@@ -170,35 +217,38 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                      float *state_out, ET *__restrict__ y,
                      int T, int Hk, int Hv, int xcd_group, float scale, int flags)
 {
-    using L = WyCfg<ET>;
+    using L = WyCfg<ET, NSW>;
     using X4 = typename Vec<ET>::x4;
     using X8 = typename Vec<ET>::x8;
     constexpr int C = L::C, DK = L::DK, DV = L::DV;
-    constexpr int NBT = L::NBT, NBK = L::NBK, NSK = L::NSK, NB = L::NB;
+    constexpr int NBT = L::NBT, NBK = L::NBK, NSK = L::NSK, NB = L::NB, ROWS = L::ROWS;
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     auto Gv = [&](int c) { return reinterpret_cast<float *>(smem + L::oVec + (c % 3) * L::NV * 4); };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = wave & 3;                      // state wave index, or prep wave index
-    const bool state_wave = wave < 4;
+    const bool state_wave = wave < NSW;
+    const int w = state_wave ? wave : wave - NSW; // state wave index, or prep wave index
     // Lane coordinates.  They pass through an empty asm statement at the top
     // of every chunk, so the compiler forms lane-dependent addresses inside
     // the loop instead of holding dozens of precombined addresses across it.
     int lane = tid & 63, x = lane & 15, qd = lane >> 4;
 
     // Workgroups are dealt round-robin over the 8 XCDs, so workgroups i and
-    // i + 8 share an XCD and its L2; with xcd_group = Hv/Hk > 1 they get
-    // value heads of the same key head, whose q/k stream is then fetched
-    // from HBM once per group.
+    // i + 8 share an XCD and its L2.  Workgroup r works on value rows
+    // ROWS (r % NSPLIT) .. + ROWS - 1 of slot r / NSPLIT; with xcd_group > 1
+    // the xcd_group workgroups that read the same q/k stream (the value
+    // slices of a slot, the value heads of a key head) share an XCD, so that
+    // the stream is fetched from HBM once per group.
     int bid = blockIdx.x;
     if (xcd_group > 1) {
         const int xcd = bid & 7, kk = bid >> 3;
         const int sib = kk % xcd_group, mm = kk / xcd_group;
         bid = (mm * 8 + xcd) * xcd_group + sib;
     }
-    const int b = bid / Hv, hv = value_head_of_rank(bid % Hv, Hk, Hv, flags);
+    const int slot = bid / L::NSPLIT, row0 = ROWS * (bid % L::NSPLIT);
+    const int b = slot / Hv, hv = value_head_of_rank(slot % Hv, Hk, Hv, flags);
     const int hk = key_head(hv, Hk, Hv, flags);
     const int nchunks = (T + C - 1) / C;
 
@@ -216,8 +266,9 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // 8 (jb%2) + 2048 tb; the 8 columns of blocks 2 s, 2 s + 1: ^ 64 s
     auto f_lA = [&]() { return (unsigned)(x * 128 + (((qd ^ (x >> 1)) & 7) << 4)); };
     auto aoff = [](unsigned lA, int jb, int tb) { return (lA ^ (64 * (jb >> 1))) + 8 * (jb & 1) + 2048 * tb; };
-    // V slice: transpose read rows 16 jb + r4, permuted columns 8 (m/4) + 4 vb + m%4: + 8 vb + 1024 jb
-    auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 64 + (x & 3) * 16); };
+    // V slice: transpose read rows 16 jb + r4, permuted columns 4 NB (m/4) +
+    // 4 vb + m%4: + 8 vb + 16 VRB jb
+    auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * L::VRB + (x & 3) * 8 * NB); };
     // float32 block, row fragment of row x (unit qd)
     auto f_lF = [&]() { return (unsigned)(x * 64 + ((qd ^ ((x >> 2) & 3)) << 4)); };
     // transposed 16-bit block of T: transpose read giving lane (x, qd) the
@@ -230,8 +281,10 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // 16 l of a 1 KB block), written as inline assembly so that the compiler
     // does not wait for the transfer before the wave's next LDS access; the
     // issuing waves await them with s_waitcnt vmcnt(0) before the barrier
-    // that closes the phase.  State wave w fills K rows 16 w .. 16 w + 15,
-    // prep wave 3 all of Q and prep wave 2 all of V.  The swizzle of K and Q
+    // that closes the phase.  With four state waves, state wave w fills
+    // rows 16 w .. 16 w + 15 of K and prep wave 3 all of Q; with two, prep
+    // wave 5 fills K and prep waves 3 and 4 one half of Q each.  Prep wave 2
+    // fills the V slices of all state waves.  The swizzle of K and Q
     // is applied on the source side.  Rows past the end of the sequence fetch
     // the last row again; with g = 1 and beta = 0 there, those rows add
     // nothing (their rows of A and columns of T diag(beta) vanish, so D is
@@ -239,11 +292,13 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const size_t kstride = (size_t)Hk * DK, vstride = (size_t)Hv * DV;
     const ET *kbase = k + ((size_t)b * T * Hk + hk) * DK;
     const ET *qbase = q + ((size_t)b * T * Hk + hk) * DK;
-    const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV;
+    const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV + row0;
     const float *gbase = g + (size_t)b * T * Hv + hv;
     const float *bbase = beta + (size_t)b * T * Hv + hv;
     auto f_okq0 = [&](int rg) { return (unsigned)((16 * rg + qd) * kstride + 8 * ((lane & 15) ^ qd)); };
-    auto f_ov0 = [&]() { return (unsigned)((lane >> 2) * vstride + 8 * (lane & 3)); };
+    // V: 16-byte pieces of 8 values, 2 NB pieces per token row
+    constexpr int VPR = 2 * NB, VRI = 64 / VPR;           // pieces per row, rows per load
+    auto f_ov0 = [&]() { return (unsigned)((lane / VPR) * vstride + 8 * (lane % VPR)); };
     const unsigned lds_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
     auto g2lds = [&](const ET *src, unsigned off, unsigned lds_byte) {
         const unsigned la = __builtin_amdgcn_readfirstlane(lds_base + lds_byte);
@@ -268,20 +323,20 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
         }
     };
-    // value columns 32 sl .. 32 sl + 31 of a V chunk
+    // the value columns of state wave sl (16 NB of them) of a V chunk
     auto issue_v = [&](int c, int sl) {
         const int t0 = c * C;
-        const ET *src = vbase + (size_t)t0 * vstride + 32 * sl;
+        const ET *src = vbase + (size_t)t0 * vstride + 16 * NB * sl;
         const unsigned dst = L::oV + sl * L::VSL;
         if (t0 + C <= T) {
             const unsigned o0 = f_ov0();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g2lds(src, 2 * (o0 + 16 * i * (unsigned)vstride), dst + 1024 * i);
+            for (int i = 0; i < C / VRI; ++i) g2lds(src, 2 * (o0 + VRI * i * (unsigned)vstride), dst + 1024 * i);
         } else {
             const int last = T - t0 - 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                g2lds(src, 2 * (unsigned)(min(16 * i + (lane >> 2), last) * vstride + 8 * (lane & 3)), dst + 1024 * i);
+            for (int i = 0; i < C / VRI; ++i)
+                g2lds(src, 2 * (unsigned)(min(VRI * i + lane / VPR, last) * vstride + 8 * (lane % VPR)), dst + 1024 * i);
         }
     };
     // g and beta of chunk c into the staging buffer c % 2 (one wave; lane =
@@ -370,11 +425,28 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         return *reinterpret_cast<const f32x4 *>(gv + kVSfx * C + 16 * jb + 4 * qd) * mf;
     };
 
+    // QKR = R (Q K^T) / sqrt(Dk), lower including the diagonal, from tile
+    // (ib, jb) of Q K^T in registers (lane (x, qd): t = 16 ib + x, j = 16 jb
+    // + 4 qd + r)
+    auto store_qkr = [&](const float *gv, int ib, int jb, f32x4 acc) {
+        const unsigned lA = f_lA();
+        if (ib == jb) {
+            const f32x4 R = diag_ratio(gv, ib);
+            f32x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[r]) : 0.f;
+            sts4<ET>(smem, L::oQKR + aoff(lA, ib, ib), cvt4<ET>(o));
+        } else {
+            const f32x4 R = off_ratio(gv, ib, jb);
+            sts4<ET>(smem, L::oQKR + aoff(lA, jb, ib), cvt4<ET>(R * acc * scale));
+        }
+    };
+
     if (state_wave) {
         // ================= state waves =================
         f32x4 S[NBK][NB];                        // S^T tiles: rows = keys kcol, columns = values
         const size_t sbase = ((size_t)b * Hv + hv) * DV * DK;
-        auto vcol = [&](int vb, int xx) { return 32 * w + 8 * (xx >> 2) + 4 * vb + (xx & 3); };
+        auto vcol = [&](int vb, int xx) { return row0 + 16 * NB * w + 4 * NB * (xx >> 2) + 4 * vb + (xx & 3); };
         auto kcol = [&](int kb, int q4) { return 32 * (kb >> 1) + 8 * q4 + 4 * (kb & 1); };
         {
             // rows of zeros (stride 0) when there is no initial state
@@ -387,7 +459,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     S[kb][vb] = *reinterpret_cast<gf32x4 *>(sin + (size_t)vcol(vb, x) * rstride + kcol(kb, qd));
         }
         // QKR blocks above the diagonal are never written: zero the buffer once.
-        for (int i = tid; i < (int)(C * C * 2 / 16); i += 256)
+        for (int i = tid; i < (int)(C * C * 2 / 16); i += 64 * NSW)
             reinterpret_cast<uint4 *>(smem + L::oQKR)[i] = zero_u4();
 #pragma unroll
         for (int kb = 0; kb < NBK; ++kb)
@@ -396,7 +468,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // K of chunk 0, the gates of chunks 0 and 1 and the gate products
         // of chunk 0 before the pipeline starts
         if (nchunks > 0) {
-            issue_kq(kbase, L::oK, 0, w);
+            for (int rg = w; rg < NBT; rg += NSW) issue_kq(kbase, L::oK, 0, rg);
             if (w == 0) {
                 load_gb(0);
                 if (nchunks > 1) load_gb(1);
@@ -409,16 +481,18 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // at the start of phase a (they would otherwise wait at its end), and
         // wait for them before its barrier.
         auto issue_inputs = [&](int n) {
-            if (n + 2 < nchunks) issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, w);
+            if (n + 2 < nchunks)
+                for (int rg = w; rg < NBT; rg += NSW) issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, rg);
             if (w == 0 && n + 3 < nchunks) load_gb(n + 3);
         };
+        // (with two state waves, prep waves 5 and 4 issue these in the loop)
         issue_inputs(-1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                           // A, T_ii of chunk 0
         lds_barrier();                           // first blocks of T of chunk 0, Q_0, V_0
         for (int n = 0; n < nchunks; ++n) {
             asm volatile("" : "+v"(lane), "+v"(x), "+v"(qd));
-            issue_inputs(n);
+            if constexpr (NSW == 4) issue_inputs(n);
             const unsigned lKt = f_lKt(), lA = f_lA();
             const unsigned kbn = L::oK + (n % 3) * L::KBUF;
             const float *gv = Gv(n);
@@ -436,8 +510,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                     for (int vb = 0; vb < NB; ++vb) Y[vb][tb] = M[tb][vb] = zero4();
                 auto products = [&](auto W) {
-                    constexpr int wc = decltype(W)::value;
-                    constexpr int nt = wy_ntiles(wc);
+                    constexpr auto TL = qk_state<NSW>(decltype(W)::value);
+                    constexpr int nt = ntiles(TL);
                     f32x4 acc[nt];
 #pragma unroll
                     for (int i = 0; i < nt; ++i) acc[i] = zero4();
@@ -463,31 +537,24 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             }
 #pragma unroll
                         for (int i = 0; i < nt; ++i)
-                            acc[i] = mfma(fk[wy_tile_jb(wc, i)], fq[wy_tile_ib(wc, i)], acc[i]);
+                            acc[i] = mfma(fk[TL.t[i].jb], fq[TL.t[i].ib], acc[i]);
                         // one key step at a time: the 16-bit copy of the
                         // state is formed step by step, not held whole
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                    // QKR = R (Q K^T) / sqrt(Dk), lower including the diagonal
-                    {
-                        const f32x4 R = diag_ratio(gv, wc);
-                        f32x4 o;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[0][r]) : 0.f;
-                        sts4<ET>(smem, L::oQKR + aoff(lA, wc, wc), cvt4<ET>(o));
-                    }
-#pragma unroll
-                    for (int i = 1; i < nt; ++i) {
-                        const int ib = wy_tile_ib(wc, i), jb = wy_tile_jb(wc, i);
-                        const f32x4 R = off_ratio(gv, ib, jb);
-                        sts4<ET>(smem, L::oQKR + aoff(lA, jb, ib), cvt4<ET>(R * acc[i] * scale));
-                    }
+                    for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
                 };
-                switch (w) {
-                case 0: products(std::integral_constant<int, 0>{}); break;
-                case 1: products(std::integral_constant<int, 1>{}); break;
-                case 2: products(std::integral_constant<int, 2>{}); break;
-                default: products(std::integral_constant<int, 3>{}); break;
+                if constexpr (NSW == 4) {
+                    switch (w) {
+                    case 0: products(std::integral_constant<int, 0>{}); break;
+                    case 1: products(std::integral_constant<int, 1>{}); break;
+                    case 2: products(std::integral_constant<int, 2>{}); break;
+                    default: products(std::integral_constant<int, 3>{}); break;
+                    }
+                } else {
+                    if (w == 0) products(std::integral_constant<int, 0>{});
+                    else products(std::integral_constant<int, 1>{});
                 }
                 // the right-hand side E = V - G M in two 16-bit parts: V as
                 // loaded (exact) and -G M rounded once; V read with the
@@ -498,7 +565,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gv + kVG * C + 16 * tb + 4 * qd);
 #pragma unroll
                     for (int vb = 0; vb < NB; ++vb) {
-                        Vf[tb][vb] = ld_tr<ET>(smem, vsl + 8 * vb + 1024 * tb);
+                        Vf[tb][vb] = ld_tr<ET>(smem, vsl + 8 * vb + 16 * L::VRB * tb);
                         E[tb][vb] = cvt4<ET>(g4 * M[tb][vb] * -1.f);
                     }
                 }
@@ -550,7 +617,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             Y[vb][tb] = mfma(cat8<ET>(Df[2 * s][vb], Df[2 * s + 1][vb]), fr, Y[vb][tb]);
                     }
                 }
-                // y: lane (x, qd) holds token 16 tb + x, values 32 w + 8 qd + (0..7).
+                // y: lane (x, qd) holds token 16 tb + x, values vcol(vb, 4 qd + r),
+                // 4 NB consecutive ones.
                 // The stores go through a buffer resource that spans the
                 // chunk's cn valid token rows: the hardware drops those past
                 // the end of the sequence, with no branch around the stores.
@@ -560,11 +628,16 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     const unsigned rowb = (unsigned)(Hv * DV) * (unsigned)sizeof(ET);
                     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
                         (void *)(y + (((size_t)b * T + t0) * Hv + hv) * DV), (short)0, (int)(cn * rowb), 0x00020000);
+                    typedef int i32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-                    for (int tb = 0; tb < NBT; ++tb)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(i32x4, cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]))), yr,
-                            (int)((16 * tb + x) * rowb + (32 * w + 8 * qd) * sizeof(ET)), 0, 0);
+                    for (int tb = 0; tb < NBT; ++tb) {
+                        const int off = (int)((16 * tb + x) * rowb + vcol(0, 4 * qd) * sizeof(ET));
+                        if constexpr (NB == 2)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(i32x4, cat8<ET>(cvt4<ET>(Y[0][tb]), cvt4<ET>(Y[1][tb]))), yr, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, cvt4<ET>(Y[0][tb])), yr, off, 0, 0);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // S^T <- G_last S^T + K^T diag(Rl) D
@@ -619,8 +692,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             sts4<ET>(smem, blk + L::HBLK, cvt4<ET>(tu - to_f32x4<ET>(h)));
         };
         // Partial sums Z_2, Z_3 of column 0, carried from the first half of
-        // the solve (wave 0) to its second half (wave 3) in 16-byte slots
-        // indexed by lane
+        // the solve (prep wave 0) to its second half (prep wave 3, or 4 with
+        // six prep waves) in 16-byte slots indexed by lane
         auto zst = [&](int i, f32x4 v) { *reinterpret_cast<f32x4 *>(smem + L::oZ + i * L::FBLK + 16 * lane) = v; };
         auto zld = [&](int i) { return *reinterpret_cast<const f32x4 *>(smem + L::oZ + i * L::FBLK + 16 * lane); };
         // iteration n: phase a finishes T of chunk n and builds A, T_ii of
@@ -628,15 +701,22 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         // start).  The blocks below the diagonal, with -A stored:
         //   Z_i = sum_{j<=k<i} (-A_ik) T_kj,  T_ij = T_ii Z_i,
         // every product in float32 on the matrix cores.  First half (phase
-        // b, wave p = column p): column 0 up to T_10 and the terms of Z_2,
-        // Z_3 through T_10; columns 1 and 2 whole.  Second half (phase a of
-        // the next iteration, wave 3): T_20, T_30.
+        // b, prep wave p = column p): column 0 up to T_10 and the terms of
+        // Z_2, Z_3 through T_10; columns 1 and 2 whole.  Second half (phase a
+        // of the next iteration, prep wave 3 or 4): T_20, T_30.
         for (int n = -1; n < nchunks; ++n) {
             const int m = n + 1;
             const unsigned lF = f_lF();
             auto ff = [&](unsigned base) { return *reinterpret_cast<const f32x4 *>(smem + base + lF); };
             // ---------------- phase a ----------------
-            if (n >= 0 && p == 3) {
+            if constexpr (NSW == 2) {
+                // with two state waves, prep wave 5 loads K two chunks ahead
+                // and the gates three ahead (the state waves do with four)
+                if (p == 5 && n >= 0 && n + 2 < nchunks)
+                    for (int rg = 0; rg < NBT; ++rg) issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, rg);
+                if (p == 5 && n >= 0 && n + 3 < nchunks) load_gb(n + 3);
+            }
+            if (n >= 0 && p == (NSW == 4 ? 3 : 4)) {
                 const unsigned ab = L::oA + (n & 1) * L::ABUF;
                 const f32x4 t20 = mma_f32(ff(ab + L::bTd + 2 * L::FBLK), zld(0), zero4());
                 const f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 2) * L::FBLK), t20, zld(1));
@@ -651,8 +731,9 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 const unsigned lKt = f_lKt();
                 const float *gv = Gv(m);
                 auto kk_tiles = [&](auto W) {
-                    constexpr int wc = decltype(W)::value;
-                    constexpr int nt = kk_ntiles(wc);
+                    constexpr auto TL = kk_prep<NSW>(decltype(W)::value);
+                    constexpr int nt = ntiles(TL);
+                    if constexpr (nt > 0) {
                     f32x4 acc[nt];
 #pragma unroll
                     for (int i = 0; i < nt; ++i) acc[i] = zero4();
@@ -661,31 +742,37 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         const unsigned lo = lKt ^ (64 * s);
 #pragma unroll
                         for (int i = 0; i < nt; ++i)
-                            acc[i] = mfma(lds8<ET>(smem, kbm + lo + 4096 * kk_tile_jb(wc, i)),
-                                          lds8<ET>(smem, kbm + lo + 4096 * kk_tile_ib(wc, i)), acc[i]);
-                    }
-                    {
-                        const int t = 16 * wc + x;
-                        const float bt = gv[kVb * C + t];
-                        const f32x4 R = diag_ratio(gv, wc);
-                        f32x4 a;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[0][r]) : 0.f;
-                        *reinterpret_cast<f32x4 *>(smem + L::oAd + (t * L::LDD + 4 * qd) * 4) = a;
+                            acc[i] = mfma(lds8<ET>(smem, kbm + lo + 4096 * TL.t[i].jb),
+                                          lds8<ET>(smem, kbm + lo + 4096 * TL.t[i].ib), acc[i]);
                     }
 #pragma unroll
-                    for (int i = 1; i < nt; ++i) {
-                        const int ib = kk_tile_ib(wc, i), jb = kk_tile_jb(wc, i);
-                        const f32x4 R = off_ratio(gv, ib, jb);
+                    for (int i = 0; i < nt; ++i) {
+                        const int ib = TL.t[i].ib, jb = TL.t[i].jb;
                         const float bt = gv[kVb * C + 16 * ib + x];
-                        *reinterpret_cast<f32x4 *>(smem + ab + wy_aidx(ib, jb) * L::FBLK + lF) = R * acc[i] * (-bt);
+                        if (ib == jb) {
+                            const f32x4 R = diag_ratio(gv, ib);
+                            f32x4 a;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[i][r]) : 0.f;
+                            *reinterpret_cast<f32x4 *>(smem + L::oAd + ((16 * ib + x) * L::LDD + 4 * qd) * 4) = a;
+                        } else {
+                            const f32x4 R = off_ratio(gv, ib, jb);
+                            *reinterpret_cast<f32x4 *>(smem + ab + wy_aidx(ib, jb) * L::FBLK + lF) = R * acc[i] * (-bt);
+                        }
+                    }
                     }
                 };
                 switch (p) {
                 case 0: kk_tiles(std::integral_constant<int, 0>{}); break;
                 case 1: kk_tiles(std::integral_constant<int, 1>{}); break;
                 case 2: kk_tiles(std::integral_constant<int, 2>{}); break;
-                default: kk_tiles(std::integral_constant<int, 3>{}); break;
+                case 3: kk_tiles(std::integral_constant<int, 3>{}); break;
+                default:
+                    if constexpr (NSW == 2) {
+                        if (p == 4) kk_tiles(std::integral_constant<int, 4>{});
+                        else kk_tiles(std::integral_constant<int, 5>{});
+                    }
+                    break;
                 }
                 // T_pp = (I + A_pp)^-1 by float32 forward substitution: four
                 // lanes per column c, lane part pt holding rows pt, pt+4,
@@ -694,7 +781,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 // come from this wave's own writes above (LDS keeps a wave's
                 // accesses in order).
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                {
+                if (p < NBT) {
                     const int base = 16 * p;
                     const int pt = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
                     const float *ad = reinterpret_cast<const float *>(smem + L::oAd);
@@ -732,22 +819,57 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
                 }
             }
+            if constexpr (NSW == 2) {
+                // with two state waves, prep waves 0 and 1 compute four of
+                // the Q K^T tiles of chunk n
+                if (n >= 0 && p < 2) {
+                    const unsigned kbn = L::oK + (n % 3) * L::KBUF, lKt = f_lKt();
+                    const float *gv = Gv(n);
+                    auto qk_tiles = [&](auto W) {
+                        constexpr auto TL = qk_prep<NSW>(decltype(W)::value);
+                        constexpr int nt = ntiles(TL);
+                        f32x4 acc[nt];
+#pragma unroll
+                        for (int i = 0; i < nt; ++i) acc[i] = zero4();
+#pragma unroll
+                        for (int s = 0; s < NSK; ++s) {
+                            const unsigned lo = lKt ^ (64 * s);
+#pragma unroll
+                            for (int i = 0; i < nt; ++i)
+                                acc[i] = mfma(lds8<ET>(smem, kbn + lo + 4096 * TL.t[i].jb),
+                                              lds8<ET>(smem, L::oQ + lo + 4096 * TL.t[i].ib), acc[i]);
+                        }
+#pragma unroll
+                        for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
+                    };
+                    if (p == 0) qk_tiles(std::integral_constant<int, 0>{});
+                    else qk_tiles(std::integral_constant<int, 1>{});
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
             lds_barrier();
             // ---------------- phase b ----------------
             if (m < nchunks) {
                 // Q and V of chunk m (their buffers were last read in phase
-                // a): prep waves 3 and 2, whose blocks of T need the least work
+                // a): prep waves 3 (and 4) and 2, whose blocks of T need the
+                // least work
                 if (p == 3) {
 #pragma unroll
-                    for (int rg = 0; rg < 4; ++rg) issue_kq(qbase, L::oQ, m, rg);
+                    for (int rg = 0; rg < (NSW == 4 ? 4 : 2); ++rg) issue_kq(qbase, L::oQ, m, rg);
+                } else if (NSW == 2 && p == 4) {
+#pragma unroll
+                    for (int rg = 2; rg < 4; ++rg) issue_kq(qbase, L::oQ, m, rg);
                 } else if (p == 2) {
 #pragma unroll
-                    for (int sl = 0; sl < 4; ++sl) issue_v(m, sl);
+                    for (int sl = 0; sl < NSW; ++sl) issue_v(m, sl);
                 }
                 const unsigned ab = L::oA + (m & 1) * L::ABUF;
-                const f32x4 tpp = ff(ab + L::bTdT + p * L::FBLK);   // T_pp, lane (x, qd): rows 4 qd .., column x
-                emit(m, p, p, tpp);
+                if (p < NBT) {
+                    const f32x4 tpp = ff(ab + L::bTdT + p * L::FBLK);   // T_pp, lane (x, qd): rows 4 qd .., column x
+                    emit(m, p, p, tpp);
+                }
                 if (p == 0) {
+                    const f32x4 tpp = ff(ab + L::bTdT);
                     const f32x4 z1 = mma_f32(ff(ab + wy_aidx(1, 0) * L::FBLK), tpp, zero4());
                     f32x4 z2 = mma_f32(ff(ab + wy_aidx(2, 0) * L::FBLK), tpp, zero4());
                     f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 0) * L::FBLK), tpp, zero4());
@@ -758,6 +880,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     zst(1, z3);
                     emit(m, 1, 0, t10);
                 } else if (p == 1) {
+                    const f32x4 tpp = ff(ab + L::bTdT + 1 * L::FBLK);
                     const f32x4 z2 = mma_f32(ff(ab + wy_aidx(2, 1) * L::FBLK), tpp, zero4());
                     f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 1) * L::FBLK), tpp, zero4());
                     const f32x4 t21 = mma_f32(ff(ab + L::bTd + 2 * L::FBLK), z2, zero4());
@@ -765,6 +888,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     emit(m, 2, 1, t21);
                     emit(m, 3, 1, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
                 } else if (p == 2) {
+                    const f32x4 tpp = ff(ab + L::bTdT + 2 * L::FBLK);
                     const f32x4 z3 = mma_f32(ff(ab + wy_aidx(3, 2) * L::FBLK), tpp, zero4());
                     emit(m, 3, 2, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
                 }

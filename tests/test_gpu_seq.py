@@ -162,3 +162,25 @@ def test_auto_chunk(gpu_lib, dtype, D):
         torch.cuda.synchronize()
         yr, sr = oracle_run(inp)
         assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, dtype, f"auto {dtype} T={T}")
+
+
+@pytest.mark.parametrize("B,Hk,Hv", [(2, 16, 32), (5, 13, 13), (4, 16, 32), (1, 43, 129), (8, 16, 32), (1, 257, 257)],
+                         ids=["64slots", "65slots", "128slots", "129slots", "256slots", "257slots"])
+def test_auto_chunk_slots(gpu_lib, B, Hk, Hv):
+    """C = 0 with 16-bit inputs and 128-dimensional heads on both sides of
+    the slot-count switches of the chunk length (64 / 65, 128 / 129, 256 /
+    257 slots) at lengths where the choice depends on them; sampled slots."""
+    for T in (48, 96, 128):
+        inp = gi.make_inputs(B, T, Hk, Hv, 128, 128, "bf16", gate="sigmoid", state_std=0.1, seed=B * Hv + T)
+        d = upload(inp)
+        y, s = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=0)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(B * Hv + T)
+        mask = np.zeros((B, Hv), bool)
+        mask.reshape(-1)[rng.choice(B * Hv, 6, replace=False)] = True
+        mask[-1, -1] = True
+        yr, sr = oracle_run(inp, slot_mask=mask)
+        ym = np.broadcast_to(mask[:, None, :, None], yr.shape)
+        sm = np.broadcast_to(mask[:, :, None, None], sr.shape)
+        assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, "bf16", f"auto B={B} Hk={Hk} Hv={Hv} T={T}",
+                      y_mask=ym, s_mask=sm)

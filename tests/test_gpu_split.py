@@ -1,9 +1,11 @@
-"""GPU parity of the generic chunk kernel's value-slice split against the f64
-oracle.  With few (batch, value-head) slots the kernel runs Dv / DVS
+"""GPU parity of the chunk kernels' value-slice split against the f64
+oracle.  With few (batch, value-head) slots the generic kernel runs Dv / DVS
 workgroups per slot (4 or 2 slices of the value columns, each recomputing
-the chunk's C x C work); the cases sit on both sides of every slot-count
-threshold of the split, with ragged lengths, grouped and tiled heads,
-Dk != Dv and every dtype.  Large grids are checked on sampled slots.
+the chunk's C x C work), and the pipelined 64-token kernel (16-bit inputs,
+Dk = Dv = 128) four workgroups of 32 value rows; the cases sit on both
+sides of every slot-count threshold of the split, with ragged lengths,
+grouped and tiled heads, Dk != Dv and every dtype.  Large grids are checked
+on sampled slots.
 """
 import numpy as np
 import pytest
@@ -31,11 +33,21 @@ CASES = [
     ("f32", 2, 8, 64, 128, 128, 16, 35, 2),     # 128 slots
     ("f32", 1, 3, 129, 128, 128, 16, 35, 1),    # 129 slots (Hv / Hk = 43)
     ("f32", 1, 4, 8, 128, 128, 32, 35, 1),      # C = 32 is not split in f32
+    # the pipelined kernel (C = 64)
+    ("bf16", 1, 8, 8, 128, 128, 64, 150, 4),    # 8 slots
+    ("bf16", 2, 16, 32, 128, 128, 64, 200, 4),  # 64 slots, grouped heads
+    ("bf16", 5, 13, 13, 128, 128, 64, 130, 1),  # 65 slots
+    ("bf16", 3, 11, 22, 128, 128, 64, 70, 1),   # 66 slots, grouped heads
+    ("f16", 1, 3, 3, 128, 128, 64, 129, 4),     # 3 slots
+    ("f16", 4, 8, 16, 128, 128, 64, 77, 4),     # 64 slots
+    ("f16", 1, 5, 65, 128, 128, 64, 64, 1),     # 65 slots (Hv / Hk = 13)
 ]
 
 
-def expected_split(dt, Dv, C, slots):
+def expected_split(dt, Dk, Dv, C, slots):
     """The slot-count rule of the dispatcher, restated for the cases above."""
+    if C == 64 and dt != "f32" and Dk == 128 and Dv == 128:
+        return 4 if slots <= 64 else 1
     if Dv == 128:
         if dt == "f32":
             return 2 if (C == 16 and slots <= 128) else 1
@@ -51,7 +63,7 @@ def expected_split(dt, Dv, C, slots):
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-B{c[1]}-Hk{c[2]}-Hv{c[3]}-D{c[4]}x{c[5]}-C{c[6]}-T{c[7]}")
 def test_split(gpu_lib, case, heads):
     dt, B, Hk, Hv, Dk, Dv, C, T, nsplit = case
-    assert expected_split(dt, Dv, C, B * Hv) == nsplit
+    assert expected_split(dt, Dk, Dv, C, B * Hv) == nsplit
     if heads == "tiled" and Hk == Hv:
         pytest.skip("the two head maps coincide when Hk = Hv")
     inp = gi.make_inputs(B, T, Hk, Hv, Dk, Dv, dt, gate="sigmoid", state_std=0.1, seed=B * 1000 + Hv + T)
