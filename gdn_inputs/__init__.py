@@ -21,7 +21,13 @@ Recipe (one ``numpy.random.default_rng(seed)`` per call, PCG64):
   ``"sigmoid"``   g = sigmoid(x),        x ~ N(2, 1)   (decays 0.73..0.95)
   ``"uniform"``   g ~ U[lo, hi)
   ``"const"``     g = a given constant (used for underflow cases)
-* beta = sigmoid(N(0, 1));
+* beta = sigmoid(N(0, 1)), or a given constant;
+* with ``key_corr = rho``, every key of a (batch, key head) is
+  normalise(k_0 + rho * n_t): one shared direction k_0 (drawn from a second
+  generator, ``default_rng([seed, 1])``, so that the main draws are the same
+  as without it) plus the usual per-token draw n_t scaled by rho.  Small rho
+  gives nearly parallel keys, the hard case of the chunk's triangular system
+  (with beta near 1 and g = 1 its rows nearly cancel);
 * state_in ~ N(0, sigma) with sigma the standard deviation, or zeros, or None;
 * float64 values are stored as float32 (round to nearest even, numpy's
   cast), then as bf16 (round to nearest even on the float32 bits) or as
@@ -123,7 +129,8 @@ def _softplus(x: np.ndarray) -> np.ndarray:
 
 def make_inputs(B, T, Hk, Hv, Dk, Dv, dtype="bf16", *, gate="softplus",
                 gate_lo=0.95, gate_hi=1.0, gate_const=None, state_std=0.05,
-                state=True, normalise_qk=True, seed=0, **_ignored):
+                state=True, normalise_qk=True, key_corr=None, beta_const=None,
+                seed=0, **_ignored):
     """Draw one seeded input set.
 
     Returns a dict with ``q, k, v`` (stored dtype), ``g, beta`` (float32),
@@ -136,6 +143,9 @@ def make_inputs(B, T, Hk, Hv, Dk, Dv, dtype="bf16", *, gate="softplus",
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, T, Hk, Dk))
     k = rng.standard_normal((B, T, Hk, Dk))
+    if key_corr is not None:
+        k0 = np.random.default_rng([seed, 1]).standard_normal((B, 1, Hk, Dk))
+        k = k0 / np.sqrt(np.sum(k0 * k0, axis=-1, keepdims=True)) * np.sqrt(Dk) + float(key_corr) * k
     if normalise_qk:
         q = _l2_normalise(q)
         k = _l2_normalise(k)
@@ -155,6 +165,8 @@ def make_inputs(B, T, Hk, Hv, Dk, Dv, dtype="bf16", *, gate="softplus",
         else:
             raise ValueError(f"unknown gate {gate!r}")
     beta = _sigmoid(rng.standard_normal((B, T, Hv)))
+    if beta_const is not None:
+        beta = np.full((B, T, Hv), float(beta_const))
     s = rng.standard_normal((B, Hv, Dv, Dk)) * state_std
     if state_std == 0:
         s = np.zeros_like(s)

@@ -87,7 +87,11 @@ enum {
  *               T - C*floor(T/C) tokens is handled inside the kernel), or 0:
  *               let the library choose, for this shape and T, between the
  *               sequential kernel of gdn_seq_fwd (short T) and the chunked
- *               kernel with a chunk length of its own choice.
+ *               kernel with a chunk length of its own choice.  float32
+ *               inputs run chunks of at most 32 tokens: C = 64 is served as
+ *               C = 32 (same result, as C never changes it beyond float
+ *               association; the chunk's products run at the float32 MFMA
+ *               rate, where 64-token chunks do not pay).
  *   dtype       storage type of q, k, v, y.
  *   stream      HIP stream (NULL = default stream).
  * Returns GDN_OK or a GDN_ERR_* code.

@@ -30,6 +30,11 @@ def test_tiny_f32(gpu_lib, gate, C):
     y, s = run_chunk(gpu_lib, inp, C)
     yr, sr = oracle_run(inp)
     assert_parity(y, s, yr, sr, "f32", f"tiny_f32 gate={gate} C={C}")
+    if C == 64:
+        # float32 inputs are served in chunks of at most 32 tokens: C = 64
+        # runs the C = 32 kernel, bit for bit
+        y32, s32 = run_chunk(gpu_lib, inp, 32)
+        assert np.array_equal(y, y32) and np.array_equal(s, s32)
 
 
 @pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
@@ -176,12 +181,47 @@ def test_deterministic(gpu_lib):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("heads", [(16, 32), (32, 32)])
 def test_sweep(gpu_lib, dtype, heads):
-    """Lengths 1, 7, 16, 257 and batch 1 and 2 at Dk = Dv = 128."""
+    """Lengths 1, 7, 16, 257, 1111 and batch 1 and 2 at Dk = Dv = 128 (the
+    validation matrix of the MLX page's "Validation" section: heads x dtype
+    x length x batch); at 1111 tokens on sampled slots."""
     hk, hv = heads
-    for T in (1, 7, 16, 257):
+    for T in (1, 7, 16, 257, 1111):
         for B in (1, 2):
             inp = gi.make_inputs(B, T, hk, hv, 128, 128, dtype, gate="sigmoid", state_std=0.3,
                                  seed=1000 + T + B)
             y, s = run_chunk(gpu_lib, inp, 64)
-            yr, sr = oracle_run(inp)
-            assert_parity(y, s, yr, sr, dtype, f"sweep {dtype} H={heads} T={T} B={B}")
+            mask = ym = sm = None
+            if T > 1000:
+                mask = np.zeros((B, hv), bool)
+                mask[0, 0] = mask[-1, hv - 1] = mask[B // 2, hv // 3] = True
+                ym = np.broadcast_to(mask[:, None, :, None], y.shape)
+                sm = np.broadcast_to(mask[:, :, None, None], s.shape)
+            yr, sr = oracle_run(inp, slot_mask=mask)
+            assert_parity(y, s, yr, sr, dtype, f"sweep {dtype} H={heads} T={T} B={B}", ym, sm)
+
+
+# (dtype, B, Hk, Hv, C): the pipelined kernel with four state waves (more
+# than 64 slots) and with the value split (up to 64), the generic kernel
+@pytest.mark.parametrize("case", [("bf16", 1, 35, 70, 64), ("f16", 1, 35, 70, 64),
+                                  ("bf16", 1, 2, 4, 64), ("f16", 2, 2, 2, 64),
+                                  ("bf16", 1, 2, 4, 32), ("f16", 1, 2, 4, 32)],
+                         ids=lambda c: f"{c[0]}-B{c[1]}-Hk{c[2]}-Hv{c[3]}-C{c[4]}")
+def test_correlated_keys(gpu_lib, case):
+    """Nearly parallel keys (every key of a head within a few degrees of one
+    direction), beta = 0.99 and no decay over 1111 tokens: the rows of each
+    chunk's triangular system nearly cancel and the state keeps everything
+    it is told, the case where a solve carried in 16-bit precision loses
+    most."""
+    dt, B, Hk, Hv, C = case
+    inp = gi.make_inputs(B, 1111, Hk, Hv, 128, 128, dt, gate="const", gate_const=1.0, beta_const=0.99,
+                         key_corr=0.1, state_std=0.05, seed=31 + Hv + C)
+    y, s = run_chunk(gpu_lib, inp, C)
+    mask = ym = sm = None
+    if B * Hv > 8:
+        mask = np.zeros((B, Hv), bool)
+        mask[0, 0] = mask[0, 37] = mask[-1, Hv - 1] = True
+        ym = np.broadcast_to(mask[:, None, :, None], y.shape)
+        sm = np.broadcast_to(mask[:, :, None, None], s.shape)
+    yr, sr = oracle_run(inp, slot_mask=mask)
+    assert_parity(y, s, yr, sr, dt, f"correlated keys {dt} B={B} Hk={Hk} Hv={Hv} C={C}", ym, sm)
+    assert np.isfinite(y).all() and np.isfinite(s).all()

@@ -32,8 +32,12 @@ def chained_steps(gdn, d, state_inplace=True):
     return torch.stack(ys, 1), st
 
 
-def test_decode_chained(gpu_lib):
-    inp = gi.workload_inputs("decode")
+@pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
+def test_decode_chained(gpu_lib, gate):
+    """The decode workload (256 chained steps, state in HBM) with both
+    readings of the printed gate draw: g = exp(-softplus(x)) as printed and
+    g = sigmoid(x)."""
+    inp = gi.workload_inputs("decode", gate=gate, seed=0 if gate == "softplus" else 1)
     d = upload(inp)
     y, s = chained_steps(gpu_lib, d)
     B, Hv = 64, 32
@@ -44,12 +48,12 @@ def test_decode_chained(gpu_lib):
     yg, sg = to_host_f64(y), to_host_f64(s)
     ymask = np.broadcast_to(mask[:, None, :, None], yg.shape)
     smask = np.broadcast_to(mask[:, :, None, None], sg.shape)
-    assert_parity(yg, sg, yr, sr, "f16", "decode 256 chained steps (6 slots)", ymask, smask)
+    assert_parity(yg, sg, yr, sr, "f16", f"decode 256 chained steps (6 slots) gate={gate}", ymask, smask)
     assert np.isfinite(yg).all() and np.isfinite(sg).all()
     # the chunk kernel over the same 256 tokens agrees with the oracle too
     yc, sc = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=64)
     torch.cuda.synchronize()
-    assert_parity(to_host_f64(yc), to_host_f64(sc), yr, sr, "f16", "chunk over decode tokens",
+    assert_parity(to_host_f64(yc), to_host_f64(sc), yr, sr, "f16", f"chunk over decode tokens gate={gate}",
                   ymask, smask)
 
 
