@@ -6,10 +6,12 @@
 A step is one ``gdn_chunk_fwd`` over the long-prefill workload (B=8,
 T=8192, Hk=16, Hv=32, Dk=Dv=128, C=64, bf16 q/k/v/y, f32 g/beta/state), with
 seeded synthetic inputs already resident in HBM.  W untimed steps, then K
-timed steps bracketed by ``torch.cuda.synchronize()``.  The default W = 60
-(about 30 ms of work) lets the GPU reach its sustained clock: after the
-first dozen launches the same kernel runs about 20% faster.  One JSON line is
-printed with:
+timed steps bracketed by ``torch.cuda.synchronize()``.  The secondary
+measurements below (decode, a few tokens per call, the small workloads, and
+last the vector-gate prefill on the same resident inputs, about 40 ms of
+back-to-back launches) run first, so that the timed steps start on the
+GPU's sustained clock whatever W is (the first dozen launches on an idle GPU
+run about 10-20% slower).  One JSON line is printed with:
 
 * ``value``       prefill tokens/s (B*T per step);
 * ``roofline``    the chunk kernel against the HBM roofline (it is
@@ -21,8 +23,11 @@ printed with:
 * ``roofline_mfma`` the same launch as algorithmic FLOP/s against the dense
                   bf16 MFMA peak;
 * ``decode``      256 chained ``gdn_step`` launches on the decode workload
-                  (B=64, Hk=16, Hv=32, Dk=Dv=128, fp16 I/O, f32 state in
-                  place): state GB/s and total GB/s against 8 TB/s;
+                  (B=64, Hk=16, Hv=32, Dk=Dv=128, fp16 I/O, f32 state):
+                  state GB/s and total GB/s against 8 TB/s, the roofline
+                  from steps that each read their state from HBM (state
+                  ping-ponged, the last-level cache flushed between steps),
+                  and the in-place chain for comparison;
 * ``vector_gate`` the long prefill with a decay per key dimension (g
                   [B,T,Hv,Dk], seeded U[0.95, 1) on the device): launch time
                   of the vector-gate chunk kernel (C = 32) and its HBM rate;
@@ -69,7 +74,7 @@ CHUNK_KERNEL_SOURCES = ["gdn_chunk_wy.h", "gdn_chunk_impl.h", "gdn_chunk_dispatc
                         "gdn_device.h", "gdn_chunk_bf16.hip"]
 # the kernel that runs the long-prefill workload (bf16, Dk = Dv = 128, C = 64)
 CHUNK_KERNEL = "chunk_wy_kernel"
-CHUNK_KERNEL_LABEL = "chunk_wy_kernel<bf16> (Dk=Dv=128, C=64)"
+CHUNK_KERNEL_LABEL = "chunk_wy_kernel<bf16, 4 state waves> (Dk=Dv=128, C=64)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_long_prefill_hbm_traffic.json")
 
 
@@ -342,99 +347,7 @@ def main():
     y = torch.empty_like(v)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        gdn.chunk_fwd(q, k, v, g, beta, s_in, C=P["C"], state_out=s_out, y=y, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    ms_per_step = wall * 1e3 / args.steps
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    tokens = P["B"] * P["T"]
-    nbytes = prefill_bytes(**P)
-    nflops = prefill_flops(**P)
-    achieved_gbs = nbytes / avg_launch_s / 1e9
-    traffic = load_traffic()
-
-    out = {
-        "metric": METRIC,
-        "value": tokens / (ms_per_step / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g U[0.95,1), "
-                "beta sigmoid(N(0,1)), state N(0,0.05))",
-        "config": {"workload": "long_prefill", "B": P["B"], "T": P["T"], "Hk": P["Hk"],
-                   "Hv": P["Hv"], "Dk": P["Dk"], "Dv": P["Dv"], "C": P["C"]},
-        "roofline": {
-            "kernel": CHUNK_KERNEL_LABEL,
-            "bound": "hbm",
-            "achieved": achieved_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes,
-            "launch_us_avg": avg_launch_s * 1e6,
-            "launch_us_min": min(launch_ms) * 1e3,
-        },
-        "roofline_mfma": {
-            "achieved": nflops / avg_launch_s / 1e12,
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": nflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS,
-            "algorithmic_flops_per_launch": nflops,
-        },
-    }
-    # ---------------- the long prefill with a decay per key dimension
-    if not args.no_vector_gate:
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(0)
-        gvec = 0.95 + 0.05 * torch.rand((P["B"], P["T"], P["Hv"], P["Dk"]), generator=gen, device=dev)
-        s_vg = torch.empty_like(s_in)
-        call = lambda: gdn.chunk_fwd(q, k, v, gvec, beta, s_in, C=32, state_out=s_vg, y=y, stream=stream)
-        call()
-        torch.cuda.synchronize()
-        n = 5
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us_vg = e0.elapsed_time(e1) * 1e3 / n
-        vg_bytes = prefill_bytes(**P) + 4 * P["B"] * P["T"] * P["Hv"] * (P["Dk"] - 1)
-        out["vector_gate"] = {
-            "workload": "long prefill with a decay per key dimension (g [B,T,Hv,Dk] f32, U[0.95,1))",
-            "kernel": "chunk_vg_kernel<bf16,128,128,32>", "C": 32,
-            "us_per_launch": us_vg, "tokens_per_s": P["B"] * P["T"] / (us_vg * 1e-6),
-            "hbm_GBps": vg_bytes / (us_vg * 1e-6) / 1e9,
-            "hbm_frac": vg_bytes / (us_vg * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "vs_scalar_gate": us_vg / out["roofline"]["launch_us_avg"],
-            "bytes_per_launch": vg_bytes,
-        }
-        del gvec, s_vg
-        torch.cuda.empty_cache()
-
-    del q, k, v, g, beta, y, s_out
-    torch.cuda.empty_cache()
-
+    out = {}
     # ---------------- decode
     if not args.no_decode:
         D = DECODE
@@ -484,21 +397,22 @@ def main():
         out["decode"] = {
             "workload": "decode", "B": D["B"], "Hk": D["Hk"], "Hv": D["Hv"], "Dk": D["Dk"],
             "Dv": D["Dv"], "dtype": "f16", "chained_steps": nsteps,
-            "us_per_step": us_step,
-            "state_GBps": sbytes / (us_step * 1e-6) / 1e9,
-            "total_GBps": tbytes / (us_step * 1e-6) / 1e9,
-            "roofline": {"bound": "hbm", "achieved": tbytes / (us_step * 1e-6) / 1e9,
+            "us_per_step": us_flushed,
+            "state_GBps": sbytes / (us_flushed * 1e-6) / 1e9,
+            "total_GBps": tbytes / (us_flushed * 1e-6) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": tbytes / (us_flushed * 1e-6) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": tbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS},
-            "launches": "plain back-to-back launches, state updated in place",
-            "note": "the 128 MiB state fits in the 256 MB last-level cache between steps",
-            "flushed": {
-                "us_per_step": us_flushed,
-                "state_GBps": sbytes / (us_flushed * 1e-6) / 1e9,
-                "total_GBps": tbytes / (us_flushed * 1e-6) / 1e9,
-                "frac": tbytes / (us_flushed * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                "method": "state ping-pongs between two buffers; 512 MiB scratch read "
-                          "between steps; each step timed alone with HIP events",
+                         "frac": tbytes / (us_flushed * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "method": "state ping-pongs between two buffers; 512 MiB scratch read between "
+                      "steps (every step reads its state from HBM); each step timed alone "
+                      "with HIP events",
+            "in_place": {
+                "us_per_step": us_step,
+                "state_GBps": sbytes / (us_step * 1e-6) / 1e9,
+                "total_GBps": tbytes / (us_step * 1e-6) / 1e9,
+                "frac": tbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                "launches": "plain back-to-back launches, state updated in place",
+                "note": "the 128 MiB state fits in the 256 MB last-level cache between steps",
             },
         }
         del toks, ys, st, st0, dq, dk, dv, dg, db
@@ -609,6 +523,101 @@ def main():
                       "the named C against HBM and against the MFMA peak of the input dtype",
         }
 
+    # ---------------- the long prefill with a decay per key dimension
+    if not args.no_vector_gate:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        gvec = 0.95 + 0.05 * torch.rand((P["B"], P["T"], P["Hv"], P["Dk"]), generator=gen, device=dev)
+        s_vg = torch.empty_like(s_in)
+        call = lambda: gdn.chunk_fwd(q, k, v, gvec, beta, s_in, C=32, state_out=s_vg, y=y, stream=stream)
+        call()
+        torch.cuda.synchronize()
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_vg = e0.elapsed_time(e1) * 1e3 / n
+        vg_bytes = prefill_bytes(**P) + 4 * P["B"] * P["T"] * P["Hv"] * (P["Dk"] - 1)
+        out["vector_gate"] = {
+            "workload": "long prefill with a decay per key dimension (g [B,T,Hv,Dk] f32, U[0.95,1))",
+            "kernel": "chunk_vg_kernel<bf16,128,128,32>", "C": 32,
+            "us_per_launch": us_vg, "tokens_per_s": P["B"] * P["T"] / (us_vg * 1e-6),
+            "hbm_GBps": vg_bytes / (us_vg * 1e-6) / 1e9,
+            "hbm_frac": vg_bytes / (us_vg * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_launch": vg_bytes,
+        }
+        del gvec, s_vg
+        torch.cuda.empty_cache()
+
+    # ---------------- the timed long prefill (last, on a settled clock)
+    def step():
+        gdn.chunk_fwd(q, k, v, g, beta, s_in, C=P["C"], state_out=s_out, y=y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    tokens = P["B"] * P["T"]
+    nbytes = prefill_bytes(**P)
+    nflops = prefill_flops(**P)
+    achieved_gbs = nbytes / avg_launch_s / 1e9
+    traffic = load_traffic()
+
+    out.update({
+        "metric": METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g U[0.95,1), "
+                "beta sigmoid(N(0,1)), state N(0,0.05))",
+        "config": {"workload": "long_prefill", "B": P["B"], "T": P["T"], "Hk": P["Hk"],
+                   "Hv": P["Hv"], "Dk": P["Dk"], "Dv": P["Dv"], "C": P["C"]},
+        "roofline": {
+            "kernel": CHUNK_KERNEL_LABEL,
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_us_avg": avg_launch_s * 1e6,
+            "launch_us_min": min(launch_ms) * 1e3,
+        },
+        "roofline_mfma": {
+            "achieved": nflops / avg_launch_s / 1e12,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": nflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": nflops,
+        },
+    })
+    if "vector_gate" in out:
+        out["vector_gate"]["vs_scalar_gate"] = out["vector_gate"]["us_per_launch"] / out["roofline"]["launch_us_avg"]
+    del q, k, v, g, beta, y, s_out
+    torch.cuda.empty_cache()
+
     # ---------------- CPU oracle on a bounded sample
     if not args.no_cpu_baseline:
         import oracle
@@ -640,7 +649,11 @@ def main():
                       f"on {nthreads} threads",
             "single_thread": single,
         }
-    print(json.dumps(out), flush=True)
+    head = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+            "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline")
+    ordered = {key: out[key] for key in head if key in out}
+    ordered.update({key: val for key, val in out.items() if key not in ordered})
+    print(json.dumps(ordered), flush=True)
 
 
 if __name__ == "__main__":
