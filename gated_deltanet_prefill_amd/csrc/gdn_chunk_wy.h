@@ -593,7 +593,6 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         }
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
                 // Y^T = G (S Q^T) / sqrt(Dk) + D^T QKR^T
 #pragma unroll
                 for (int tb = 0; tb < NBT; ++tb) {
@@ -639,7 +638,6 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, cvt4<ET>(Y[0][tb])), yr, off, 0, 0);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
                 // S^T <- G_last S^T + K^T diag(Rl) D
                 const unsigned lKu = f_lKu();
                 X4 Dp[NBT][NB];
