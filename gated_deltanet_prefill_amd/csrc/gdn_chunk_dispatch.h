@@ -55,13 +55,14 @@ hipError_t launch_chunk_inst(const FwdArgs &a, hipStream_t st) {
     if constexpr (sizeof(ET) == 2 && DK == 128 && DV == 128 && C == 64) {
         // the pipelined kernel: one 8-wave workgroup per slot, or, while four
         // workgroups per slot still fit the 256 CUs in one round, four
-        // workgroups of 32 value rows each (two state waves, six prep waves)
+        // 12-wave workgroups of 32 value rows each (two state waves, ten
+        // prep waves)
         const int nsplit = wy_split(nslots);
         const long nblocks = nslots * nsplit;
         const int grp = group * nsplit;          // workgroups reading one q/k stream
         const int xcd_group = (grp > 1 && nblocks % (8L * grp) == 0) ? grp : 1;
         auto kern = nsplit == 4 ? chunk_wy_kernel<ET, 2> : chunk_wy_kernel<ET, 4>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(512), 0, st,
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(nsplit == 4 ? 768 : 512), 0, st,
                            static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
                            static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                            static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, xcd_group, a.scale, a.flags);

@@ -80,7 +80,8 @@ struct WyCfg {
     static_assert(NSW_ == 4 || NSW_ == 2, "four or two state waves");
     static constexpr int C = 64, DK = 128, DV = 128;
     static constexpr int NSW = NSW_;          // state waves
-    static constexpr int NP = 8 - NSW;        // prep waves
+    static constexpr int NW = NSW == 4 ? 8 : 12;          // waves per workgroup
+    static constexpr int NP = NW - NSW;       // prep waves
     static constexpr int NB = NSW == 4 ? 2 : 1;           // value tiles per state wave
     static constexpr int ROWS = 16 * NB * NSW;            // value rows per workgroup
     static constexpr int NSPLIT = DV / ROWS;              // workgroups per slot
@@ -156,12 +157,12 @@ __device__ __forceinline__ f32x4 mma_f32(f32x4 a, f32x4 b, f32x4 acc) {
 //   K K^T, prep wave  p = 0: (0,0) (1,0) (2,0)   p = 1: (1,1) (2,1) (3,1)
 //                         p = 2: (2,2) (3,2) (3,0)   p = 3: (3,3)
 // (prep wave 3 finishes the longest column of T in the same phase).  With
-// two state and six prep waves:
-//   Q K^T, state wave w = 0: (0,0) (1,0) (2,0)   w = 1: (1,1) (2,1) (3,1)
-//          prep wave  p = 0: (2,2) (3,2)         p = 1: (3,3) (3,0)
-//   K K^T, prep wave  p = 0: (0,0)   p = 1: (1,1)   p = 2: (2,2) (1,0) (2,0)
-//                     p = 3: (3,3) (3,0) (2,1)   p = 4: (3,1) (3,2)
-// (prep wave 4 finishes the longest column of T, prep wave 5 loads K).
+// two state and ten prep waves:
+//   Q K^T, state wave w = 0: (0,0) (1,0)   w = 1: (1,1) (2,1)
+//          prep wave  p = 7: (2,0) (3,1)   p = 8: (2,2) (3,2)   p = 9: (3,3) (3,0)
+//   K K^T, prep wave  p = 0..3: (p,p)   p = 4: (1,0) (2,0)   p = 5: (3,0) (2,1)
+//                     p = 6: (3,1) (3,2)
+// (prep wave 4 finishes the longest column of T, prep waves 5 and 6 load K).
 struct Tile { int ib, jb; };
 template <int N> struct Tiles { static constexpr int n = N; Tile t[N > 0 ? N : 1]; };
 template <int NSW> constexpr auto qk_state(int w) {
@@ -173,12 +174,13 @@ template <int NSW> constexpr auto qk_state(int w) {
         default: return Tiles<3>{{{3, 3}, {3, 0}, {-1, -1}}};
         }
     }
-    return w == 0 ? Tiles<3>{{{0, 0}, {1, 0}, {2, 0}}} : Tiles<3>{{{1, 1}, {2, 1}, {3, 1}}};
+    return w == 0 ? Tiles<3>{{{0, 0}, {1, 0}, {-1, -1}}} : Tiles<3>{{{1, 1}, {2, 1}, {-1, -1}}};
 }
 template <int NSW> constexpr auto qk_prep(int p) {
-    if (NSW == 2 && p == 0) return Tiles<2>{{{2, 2}, {3, 2}}};
-    if (NSW == 2 && p == 1) return Tiles<2>{{{3, 3}, {3, 0}}};
-    return Tiles<2>{{{-1, -1}, {-1, -1}}};
+    if (NSW == 2 && p == 7) return Tiles<4>{{{2, 0}, {3, 1}, {-1, -1}, {-1, -1}}};
+    if (NSW == 2 && p == 8) return Tiles<4>{{{2, 2}, {3, 2}, {-1, -1}, {-1, -1}}};
+    if (NSW == 2 && p == 9) return Tiles<4>{{{3, 3}, {3, 0}, {-1, -1}, {-1, -1}}};
+    return Tiles<4>{{{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}}};
 }
 template <int NSW> constexpr auto kk_prep(int p) {
     if (NSW == 4) {
@@ -192,10 +194,20 @@ template <int NSW> constexpr auto kk_prep(int p) {
     switch (p) {
     case 0: return Tiles<3>{{{0, 0}, {-1, -1}, {-1, -1}}};
     case 1: return Tiles<3>{{{1, 1}, {-1, -1}, {-1, -1}}};
-    case 2: return Tiles<3>{{{2, 2}, {1, 0}, {2, 0}}};
-    case 3: return Tiles<3>{{{3, 3}, {3, 0}, {2, 1}}};
-    case 4: return Tiles<3>{{{3, 1}, {3, 2}, {-1, -1}}};
+    case 2: return Tiles<3>{{{2, 2}, {-1, -1}, {-1, -1}}};
+    case 3: return Tiles<3>{{{3, 3}, {-1, -1}, {-1, -1}}};
+    case 4: return Tiles<3>{{{1, 0}, {2, 0}, {-1, -1}}};
+    case 5: return Tiles<3>{{{3, 0}, {2, 1}, {-1, -1}}};
+    case 6: return Tiles<3>{{{3, 1}, {3, 2}, {-1, -1}}};
     default: return Tiles<3>{{{-1, -1}, {-1, -1}, {-1, -1}}};
+    }
+}
+// f(std::integral_constant<int, p>) for the runtime wave index p < N
+template <int N, typename F>
+__device__ __forceinline__ void with_wave(int p, F &&f) {
+    if constexpr (N > 0) {
+        if (p == N - 1) f(std::integral_constant<int, N - 1>{});
+        else with_wave<N - 1>(p, f);
     }
 }
 // number of real tiles (ib >= 0) in a list
@@ -210,7 +222,7 @@ constexpr int wy_aidx(int i, int j) { return i * (i - 1) / 2 + j; }
 constexpr int wy_tidx(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <typename ET, int NSW>
-__global__ __launch_bounds__(512, 1)
+__global__ __launch_bounds__(NSW == 4 ? 512 : 768, 1)
 void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                      const ET *__restrict__ v, const float *__restrict__ g,
                      const float *__restrict__ beta, const float *state_in,
@@ -512,7 +524,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 auto products = [&](auto W) {
                     constexpr auto TL = qk_state<NSW>(decltype(W)::value);
                     constexpr int nt = ntiles(TL);
-                    f32x4 acc[nt];
+                    f32x4 acc[nt > 0 ? nt : 1];
 #pragma unroll
                     for (int i = 0; i < nt; ++i) acc[i] = zero4();
 #pragma unroll
@@ -545,17 +557,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                     for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
                 };
-                if constexpr (NSW == 4) {
-                    switch (w) {
-                    case 0: products(std::integral_constant<int, 0>{}); break;
-                    case 1: products(std::integral_constant<int, 1>{}); break;
-                    case 2: products(std::integral_constant<int, 2>{}); break;
-                    default: products(std::integral_constant<int, 3>{}); break;
-                    }
-                } else {
-                    if (w == 0) products(std::integral_constant<int, 0>{});
-                    else products(std::integral_constant<int, 1>{});
-                }
+                with_wave<NSW>(w, products);
                 // the right-hand side E = V - G M in two 16-bit parts: V as
                 // loaded (exact) and -G M rounded once; V read with the
                 // permuted columns of the value tiles
@@ -708,11 +710,13 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             auto ff = [&](unsigned base) { return *reinterpret_cast<const f32x4 *>(smem + base + lF); };
             // ---------------- phase a ----------------
             if constexpr (NSW == 2) {
-                // with two state waves, prep wave 5 loads K two chunks ahead
-                // and the gates three ahead (the state waves do with four)
-                if (p == 5 && n >= 0 && n + 2 < nchunks)
-                    for (int rg = 0; rg < NBT; ++rg) issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, rg);
-                if (p == 5 && n >= 0 && n + 3 < nchunks) load_gb(n + 3);
+                // with two state waves, prep waves 5 and 6 load K two chunks
+                // ahead and prep wave 6 the gates three ahead (the state
+                // waves do with four)
+                if ((p == 5 || p == 6) && n >= 0 && n + 2 < nchunks)
+                    for (int rg = 2 * (p - 5); rg < 2 * (p - 5) + 2; ++rg)
+                        issue_kq(kbase, L::oK + ((n + 2) % 3) * L::KBUF, n + 2, rg);
+                if (p == 6 && n >= 0 && n + 3 < nchunks) load_gb(n + 3);
             }
             if (n >= 0 && p == (NSW == 4 ? 3 : 4)) {
                 const unsigned ab = L::oA + (n & 1) * L::ABUF;
@@ -760,18 +764,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
                     }
                 };
-                switch (p) {
-                case 0: kk_tiles(std::integral_constant<int, 0>{}); break;
-                case 1: kk_tiles(std::integral_constant<int, 1>{}); break;
-                case 2: kk_tiles(std::integral_constant<int, 2>{}); break;
-                case 3: kk_tiles(std::integral_constant<int, 3>{}); break;
-                default:
-                    if constexpr (NSW == 2) {
-                        if (p == 4) kk_tiles(std::integral_constant<int, 4>{});
-                        else kk_tiles(std::integral_constant<int, 5>{});
-                    }
-                    break;
-                }
+                with_wave<L::NP>(p, kk_tiles);
                 // T_pp = (I + A_pp)^-1 by float32 forward substitution: four
                 // lanes per column c, lane part pt holding rows pt, pt+4,
                 // pt+8, pt+12.  Column sweep: once x_j is final (it sits in
@@ -818,14 +811,15 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 }
             }
             if constexpr (NSW == 2) {
-                // with two state waves, prep waves 0 and 1 compute four of
-                // the Q K^T tiles of chunk n
-                if (n >= 0 && p < 2) {
+                // with two state waves, prep waves 7-9 compute the Q K^T
+                // tiles of chunk n
+                if (n >= 0 && p >= 7) {
                     const unsigned kbn = L::oK + (n % 3) * L::KBUF, lKt = f_lKt();
                     const float *gv = Gv(n);
                     auto qk_tiles = [&](auto W) {
                         constexpr auto TL = qk_prep<NSW>(decltype(W)::value);
                         constexpr int nt = ntiles(TL);
+                        if constexpr (nt > 0) {
                         f32x4 acc[nt];
 #pragma unroll
                         for (int i = 0; i < nt; ++i) acc[i] = zero4();
@@ -839,9 +833,9 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         }
 #pragma unroll
                         for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
+                        }
                     };
-                    if (p == 0) qk_tiles(std::integral_constant<int, 0>{});
-                    else qk_tiles(std::integral_constant<int, 1>{});
+                    with_wave<L::NP>(p, qk_tiles);
                 }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
@@ -849,17 +843,24 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // ---------------- phase b ----------------
             if (m < nchunks) {
                 // Q and V of chunk m (their buffers were last read in phase
-                // a): prep waves 3 (and 4) and 2, whose blocks of T need the
-                // least work
-                if (p == 3) {
+                // a): with four prep waves, prep waves 3 and 2, whose blocks
+                // of T need the least work; with ten, prep waves 7, 8 and 9
+                if constexpr (NSW == 4) {
+                    if (p == 3) {
 #pragma unroll
-                    for (int rg = 0; rg < (NSW == 4 ? 4 : 2); ++rg) issue_kq(qbase, L::oQ, m, rg);
-                } else if (NSW == 2 && p == 4) {
+                        for (int rg = 0; rg < 4; ++rg) issue_kq(qbase, L::oQ, m, rg);
+                    } else if (p == 2) {
 #pragma unroll
-                    for (int rg = 2; rg < 4; ++rg) issue_kq(qbase, L::oQ, m, rg);
-                } else if (p == 2) {
+                        for (int sl = 0; sl < NSW; ++sl) issue_v(m, sl);
+                    }
+                } else {
+                    if (p == 7 || p == 8) {
 #pragma unroll
-                    for (int sl = 0; sl < NSW; ++sl) issue_v(m, sl);
+                        for (int i = 0; i < 2; ++i) issue_kq(qbase, L::oQ, m, 2 * (p - 7) + i);
+                    } else if (p == 9) {
+#pragma unroll
+                        for (int sl = 0; sl < NSW; ++sl) issue_v(m, sl);
+                    }
                 }
                 const unsigned ab = L::oA + (m & 1) * L::ABUF;
                 if (p < NBT) {
@@ -891,7 +892,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     emit(m, 3, 2, mma_f32(ff(ab + L::bTd + 3 * L::FBLK), z3, zero4()));
                 }
             }
-            if (p == 3 && n + 2 < nchunks) scan_gates(n + 2);
+            if (p == (NSW == 4 ? 3 : 6) && n + 2 < nchunks) scan_gates(n + 2);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
