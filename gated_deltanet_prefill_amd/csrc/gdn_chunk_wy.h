@@ -527,9 +527,14 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     f32x4 acc[nt > 0 ? nt : 1];
 #pragma unroll
                     for (int i = 0; i < nt; ++i) acc[i] = zero4();
+                    X8 nq[NBT], nk[NBT];
+#pragma unroll
+                    for (int tb = 0; tb < NBT; ++tb) {
+                        nq[tb] = lds8<ET>(smem, L::oQ + lKt + 4096 * tb);
+                        nk[tb] = lds8<ET>(smem, kbn + lKt + 4096 * tb);
+                    }
 #pragma unroll
                     for (int s = 0; s < NSK; ++s) {
-                        const unsigned lo = lKt ^ (64 * s);
                         X8 fs[NB];
 #pragma unroll
                         for (int vb = 0; vb < NB; ++vb)
@@ -537,8 +542,18 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         X8 fq[NBT], fk[NBT];
 #pragma unroll
                         for (int tb = 0; tb < NBT; ++tb) {
-                            fq[tb] = lds8<ET>(smem, L::oQ + lo + 4096 * tb);
-                            fk[tb] = lds8<ET>(smem, kbn + lo + 4096 * tb);
+                            fq[tb] = nq[tb];
+                            fk[tb] = nk[tb];
+                        }
+                        // the next key step's fragments are read during this
+                        // step's products
+                        if (s + 1 < NSK) {
+                            const unsigned lo = lKt ^ (64 * (s + 1));
+#pragma unroll
+                            for (int tb = 0; tb < NBT; ++tb) {
+                                nq[tb] = lds8<ET>(smem, L::oQ + lo + 4096 * tb);
+                                nk[tb] = lds8<ET>(smem, kbn + lo + 4096 * tb);
+                            }
                         }
 #pragma unroll
                         for (int tb = 0; tb < NBT; ++tb)
