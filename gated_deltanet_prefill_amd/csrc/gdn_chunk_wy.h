@@ -51,11 +51,11 @@
 //                   products of chunk n+2; load Q_{n+1}, V_{n+1}
 //
 // LDS layouts.  K and Q have 256-byte token rows (keys along the row); the
-// 16-byte unit u of row t sits at u ^ (t % 16).  QKR has 128-byte rows, unit
+// 16-byte unit u of row t sits at u ^ kq_swz(t).  QKR has 128-byte rows, unit
 // u of row t at u ^ ((t / 2) % 8), and column j = 32 s + 16 h + 4 q + r at
 // position 32 s + 8 q + 4 h + r.  Float32 16x16 blocks (A below the
 // diagonal, T_ii by rows and by columns) have 64-byte rows, unit u of row r
-// at u ^ ((r / 4) % 4).  The expansion of T diag(beta) is stored block by
+// at u ^ ((r / 2) % 4).  The expansion of T diag(beta) is stored block by
 // block transposed (row c holds column c of the block), 32-byte rows with
 // the 8-byte piece s of row c at s ^ (2 (c / 8)), and read back as row
 // fragments with gfx950's LDS transpose load.
@@ -128,6 +128,16 @@ __device__ __forceinline__ typename Vec<ET>::x4 ld_tr(const char *smem, unsigned
         (__attribute__((address_space(3))) s16x4 *)(smem + byte));
     return __builtin_bit_cast(typename Vec<ET>::x4, raw);
 }
+// Swizzle of the 16-byte units of the K and Q rows: t % 16 with bit 3
+// flipped when bit 1 is set.  Both access kinds on these rows -- 16-byte row
+// fragments (products with the state, the Q K^T and K K^T tiles) and the
+// transpose reads of the state update (tokens along the contraction) -- are
+// then free of LDS bank conflicts on gfx950, as timed on their exact lane
+// addresses; with t % 16 alone the transpose reads take twice as long.  The
+// same holds for the float32 blocks with their swizzle keyed on (r / 2) % 4
+// rather than (r / 4) % 4.  kq_swz is linear over XOR: kq_swz(a ^ b) =
+// kq_swz(a) ^ kq_swz(b), and kq_swz(4 i) = 4 i.
+__device__ __forceinline__ int kq_swz(int t) { return (t ^ ((t & 2) << 2)) & 15; }
 template <typename ET>
 __device__ __forceinline__ typename Vec<ET>::x8 lds8(const char *smem, unsigned byte) {
     return *reinterpret_cast<const typename Vec<ET>::x8 *>(smem + byte);
@@ -266,13 +276,13 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 
     // ---- lane-dependent LDS byte offsets
     // K/Q row fragment (16 bytes at unit 4 s + qd of row 16 b + x): ^ 64 s, + 4096 b
-    auto f_lKt = [&]() { return (unsigned)(x * 256 + (((qd ^ x) & 15) << 4)); };
+    auto f_lKt = [&]() { return (unsigned)(x * 256 + ((qd ^ kq_swz(x)) << 4)); };
     // K transpose read for the state update, rows r0 + r4, keys 32 s + 4 h +
     // 8 (x%4) .. +3 (lane x then receives key 32 s + 4 h + 8 (x/4) + x%4):
     // ^ 64 s, + 8 h, + 256 r0
     auto f_lKu = [&]() {
         const int r4 = 4 * qd + (x >> 2);
-        return (unsigned)(r4 * 256 + ((((x & 3) ^ r4) & 15) << 4));
+        return (unsigned)(r4 * 256 + (((x & 3) ^ kq_swz(r4)) << 4));
     };
     // QKR rows 16 tb + x, the 4 columns 16 jb + 4 qd ..: (this ^ 64 (jb/2)) +
     // 8 (jb%2) + 2048 tb; the 8 columns of blocks 2 s, 2 s + 1: ^ 64 s
@@ -282,7 +292,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // 4 vb + m%4: + 8 vb + 16 VRB jb
     auto f_lVs = [&]() { return (unsigned)((4 * qd + (x >> 2)) * L::VRB + (x & 3) * 8 * NB); };
     // float32 block, row fragment of row x (unit qd)
-    auto f_lF = [&]() { return (unsigned)(x * 64 + ((qd ^ ((x >> 2) & 3)) << 4)); };
+    auto f_lF = [&]() { return (unsigned)(x * 64 + ((qd ^ ((x >> 1) & 3)) << 4)); };
     // transposed 16-bit block of T: transpose read giving lane (x, qd) the
     // row-x entries of columns 4 qd .. 4 qd + 3
     auto f_lT = [&]() { return (unsigned)((4 * qd + (x >> 2)) * 32 + 8 * ((x & 3) ^ ((qd >> 1) << 1))); };
@@ -307,7 +317,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     const ET *vbase = v + ((size_t)b * T * Hv + hv) * DV + row0;
     const float *gbase = g + (size_t)b * T * Hv + hv;
     const float *bbase = beta + (size_t)b * T * Hv + hv;
-    auto f_okq0 = [&](int rg) { return (unsigned)((16 * rg + qd) * kstride + 8 * ((lane & 15) ^ qd)); };
+    auto f_okq0 = [&](int rg) { return (unsigned)((16 * rg + qd) * kstride + 8 * ((lane & 15) ^ kq_swz(qd))); };
     // V: 16-byte pieces of 8 values, 2 NB pieces per token row
     constexpr int VPR = 2 * NB, VRI = 64 / VPR;           // pieces per row, rows per load
     auto f_ov0 = [&]() { return (unsigned)((lane / VPR) * vstride + 8 * (lane % VPR)); };
@@ -330,7 +340,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                 g2lds(src, 2 * ((f_okq0(rg) ^ (32 * i)) + 4 * i * (unsigned)kstride), dst + 4096 * rg + 1024 * i);
             } else {
                 const int r = 16 * rg + 4 * i + (lane >> 4);
-                g2lds(src, 2 * (unsigned)(min(r, T - t0 - 1) * kstride + 8 * ((lane & 15) ^ (r & 15))),
+                g2lds(src, 2 * (unsigned)(min(r, T - t0 - 1) * kstride + 8 * ((lane & 15) ^ kq_swz(r))),
                       dst + 4096 * rg + 1024 * i);
             }
         }
@@ -820,8 +830,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 #pragma unroll
                     for (int mm = 0; mm < 4; ++mm) {
                         const int r = pt + 4 * mm;
-                        td[r * 16 + 4 * ((c >> 2) ^ mm) + (c & 3)] = sv[mm];
-                        tdt[c * 16 + 4 * (mm ^ ((c >> 2) & 3)) + pt] = sv[mm];
+                        td[r * 16 + 4 * ((c >> 2) ^ ((r >> 1) & 3)) + (c & 3)] = sv[mm];
+                        tdt[c * 16 + 4 * (mm ^ ((c >> 1) & 3)) + pt] = sv[mm];
                     }
                 }
             }
