@@ -11,6 +11,8 @@
 //     S'_j = g S_j + d_j k
 //     y_j = (g b_j + d_j (k . q)) / sqrt(Dk)  (= S'_j . q / sqrt(Dk))
 // The three dot products finish with a butterfly over the row's 8 lanes.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -22,9 +24,11 @@ constexpr int kStepLanesPerRow = 8;
 // four value rows per lane
 constexpr long kSeqMinWaves = 2048;
 
+// (bound_ctrl set: no lane of these permutations reads outside its row, so
+// it changes nothing, and it lets the compiler fold each move into its add)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 
 // sum over the eight lanes of an aligned group (every lane gets the sum):
@@ -154,16 +158,19 @@ template <typename ET> struct RowVec<ET, 1> {
     using T = ET;
     static __device__ __forceinline__ T ld(const ET *p) { return *p; }
     static __device__ __forceinline__ float at(T v, int) { return to_f32(v); }
+    static __device__ __forceinline__ void set(T &v, int, ET x) { v = x; }
 };
 template <typename ET> struct RowVec<ET, 2> {
     using T = ET __attribute__((ext_vector_type(2)));
     static __device__ __forceinline__ T ld(const ET *p) { return *reinterpret_cast<const T *>(p); }
     static __device__ __forceinline__ float at(T v, int i) { return to_f32(v[i]); }
+    static __device__ __forceinline__ void set(T &v, int i, ET x) { v[i] = x; }
 };
 template <typename ET> struct RowVec<ET, 4> {
     using T = typename Vec<ET>::x4;
     static __device__ __forceinline__ T ld(const ET *p) { return ld4<ET>(p); }
     static __device__ __forceinline__ float at(T v, int i) { return to_f32(v[i]); }
+    static __device__ __forceinline__ void set(T &v, int i, ET x) { v[i] = x; }
 };
 
 // VG: g is [B,T,Hv,Dk]; each token first decays the state's key columns by
@@ -301,6 +308,273 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             *reinterpret_cast<f32x4 *>(state_out + row0 + (size_t)r * DK + 32 * m) = c * s[r][m];
 }
 
+// Persistent form of the sequential kernel (16-bit inputs, scalar gate, a
+// few tokens per call).  Each workgroup walks tiles of 32 R value rows; while
+// it runs the tokens of one tile, the inputs of its next tile (k, q, the
+// tile's v columns, g and beta of every token) stream into the other half of
+// a double buffer in LDS and the next tile's state rows into registers, so
+// that the state traffic of one tile overlaps the arithmetic of another.
+// Per token it is the arithmetic of seq_kernel above.
+// (the longest call it takes: from 8 tokens on the arithmetic per token,
+// not the state traffic, sets the time, and the kernel above is as fast;
+// at most 8, one token per group of eight lanes for k . q)
+constexpr int kSeqPipeMaxT = 6;
+static_assert(kSeqPipeMaxT <= 8, "k . q of one token per group of eight lanes");
+// s_waitcnt vmcnt(0) as an immediate (gfx9 encoding: vmcnt 0, expcnt and
+// lgkmcnt at their maxima), issued through the builtin so that the
+// compiler's own wait bookkeeping sees it: otherwise it assumes the state
+// registers loaded before the token loop are still in flight and waits for
+// every outstanding load, the next tile's included, before the loop
+constexpr int kVmcnt0 = 0x0F70;
+
+template <typename ET, int DK, int R>
+struct SeqPipeCfg {
+    static constexpr int ROWS = 32 * R;                   // value rows per tile
+    static constexpr int VPT = ROWS * 2 / 16;             // 16-byte pieces of v per token
+    // bytes of one input buffer for Tp token rows (Tp a multiple of 8)
+    static __host__ __device__ constexpr unsigned kq_bytes(int Tp) { return (unsigned)Tp * DK * sizeof(ET); }
+    static __host__ __device__ constexpr unsigned v_bytes(int Tp) { return (unsigned)Tp * ROWS * sizeof(ET); }
+    // (rounded up to 1 KB, the block of one load instruction)
+    static __host__ __device__ constexpr unsigned buf_bytes(int Tp) {
+        return (2 * kq_bytes(Tp) + v_bytes(Tp) + 2 * 64 * 4 + 1023) & ~1023u;
+    }
+};
+
+template <typename ET, int DK, int R>
+__global__ __launch_bounds__(256)
+void seq_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
+                     const ET *__restrict__ v, const float *__restrict__ g,
+                     const float *__restrict__ beta, const float *state_in,
+                     float *state_out, ET *__restrict__ y,
+                     int T, int Hk, int Hv, int Dv, float scale, int flags, int ntiles)
+{
+    static_assert(sizeof(ET) == 2, "16-bit inputs");
+    using L = SeqPipeCfg<ET, DK, R>;
+    using RV = RowVec<ET, R>;
+    constexpr int NP = DK / 32;                   // 16-byte state pieces per lane and row
+    constexpr int ROWS = L::ROWS;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int Tp = (T + 7) & ~7;
+    const unsigned oQ = L::kq_bytes(Tp), oV = 2 * L::kq_bytes(Tp), oG = oV + L::v_bytes(Tp), oB = oG + 256;
+    const unsigned bufb = L::buf_bytes(Tp);
+    const int tid = threadIdx.x, lane = tid & 63, sub = tid & 7;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles_per_slot = Dv / ROWS;
+    const size_t qks = (size_t)Hk * DK, vs = (size_t)Hv * Dv;
+    const unsigned lds_base = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
+    const int sstride = state_in ? DK : 0;
+
+    // inputs of tile ti into buffer bf: wave 0 the k rows, wave 1 the q rows,
+    // wave 2 the v columns, wave 3 g and beta; rows past T repeat row T - 1
+    auto issue_inputs = [&](int ti, int bf) {
+        const int slot = ti / tiles_per_slot, jt = (ti - slot * tiles_per_slot) * ROWS;
+        const int hv = slot % Hv, b = slot / Hv, hk = key_head(hv, Hk, Hv, flags);
+        const unsigned base = lds_base + (unsigned)bf * bufb;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        if (wave < 2) {
+            const ET *src = (wave == 0 ? k : q) + ((size_t)b * T * Hk + hk) * DK;
+            const unsigned dst = base + (wave == 0 ? 0u : oQ);
+            for (int i = 0; i < Tp / 4; ++i) {
+                const int tok = min(4 * i + (lane >> 4), T - 1);
+                const unsigned off = (unsigned)((tok * qks + 8 * (lane & 15)) * sizeof(ET));
+                const unsigned la = __builtin_amdgcn_readfirstlane(dst + 1024 * i);
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                             :: "v"(off), "s"(src), "s"(la) : "memory", "m0");
+            }
+        } else if (wave == 2) {
+            const ET *src = v + ((size_t)b * T * Hv + hv) * Dv + jt;
+            constexpr int TPI = 64 / L::VPT;      // tokens per instruction
+            for (int i = 0; i < Tp / TPI; ++i) {
+                const int tok = min(TPI * i + lane / L::VPT, T - 1);
+                const unsigned off = (unsigned)((tok * vs + 8 * (lane % L::VPT)) * sizeof(ET));
+                const unsigned la = __builtin_amdgcn_readfirstlane(base + oV + 1024 * i);
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                             :: "v"(off), "s"(src), "s"(la) : "memory", "m0");
+            }
+        } else {
+            const float *gs = g + (size_t)b * T * Hv + hv, *bs = beta + (size_t)b * T * Hv + hv;
+            const unsigned off = (unsigned)(min(lane, T - 1) * Hv * 4);
+            const unsigned lg = __builtin_amdgcn_readfirstlane(base + oG), lb = __builtin_amdgcn_readfirstlane(base + oB);
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                         :: "v"(off), "s"(gs), "s"(lg) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                         :: "v"(off), "s"(bs), "s"(lb) : "memory", "m0");
+        }
+#pragma clang diagnostic pop
+    };
+    // first state row of this lane's group in tile ti
+    auto row_of = [&](int ti) {
+        const int slot = ti / tiles_per_slot, jt = (ti - slot * tiles_per_slot) * ROWS;
+        return ((size_t)slot * Dv + jt + (tid >> 3) * R) * DK + 4 * sub;
+    };
+    auto load_state = [&](int ti, f32x4 (&st)[R][NP]) {
+        gfloat *sin = state_in ? (gfloat *)state_in + row_of(ti) : (gfloat *)kZeroRow + 4 * sub;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NP; ++m)
+                st[r][m] = *reinterpret_cast<gf32x4 *>(sin + (size_t)r * sstride + 32 * m);
+    };
+
+    int ti = blockIdx.x;
+    f32x4 s[R][NP], sn[R][NP];
+    issue_inputs(ti, 0);
+    load_state(ti, s);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    for (int it = 0;; ++it) {
+        const int tn = ti + (int)gridDim.x;
+        if (tn < ntiles) {
+            issue_inputs(tn, (it + 1) & 1);
+            load_state(tn, sn);
+        }
+        const int slot = ti / tiles_per_slot, jt = (ti - slot * tiles_per_slot) * ROWS;
+        const int hv = slot % Hv, b = slot / Hv;
+        ET *yp = y + ((size_t)b * T * Hv + hv) * Dv + jt + (tid >> 3) * R;
+        const char *buf = smem + (it & 1) * bufb;
+        // token t's inputs from LDS, read one token ahead
+        typename Vec<ET>::x4 kn[NP], qn[NP];
+        typename RV::T vn;
+        // the decays and betas of the tile's tokens, lane t holding token t's
+        // (one exp per token for log-space gates, not one per token and lane)
+        const float dec_l = decay_of(reinterpret_cast<const float *>(buf + oG)[lane], flags);
+        const float beta_l = reinterpret_cast<const float *>(buf + oB)[lane];
+        // k . q of token t on the eight lanes of group t (T <= 8 groups),
+        // read per token from lane 8 t
+        float kq_l = 0.f;
+        {
+            const int tq = min(tid >> 3 & 7, T - 1);
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const f32x4 kk = to_f32x4<ET>(*reinterpret_cast<const typename Vec<ET>::x4 *>(buf + (tq * DK + 32 * m + 4 * sub) * sizeof(ET)));
+                const f32x4 qq = to_f32x4<ET>(*reinterpret_cast<const typename Vec<ET>::x4 *>(buf + oQ + (tq * DK + 32 * m + 4 * sub) * sizeof(ET)));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kq_l += kk[i] * qq[i];
+            }
+            kq_l = sum8(kq_l);
+        }
+        auto lds_token = [&](int t) {
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                kn[m] = *reinterpret_cast<const typename Vec<ET>::x4 *>(buf + (t * DK + 32 * m + 4 * sub) * sizeof(ET));
+                qn[m] = *reinterpret_cast<const typename Vec<ET>::x4 *>(buf + oQ + (t * DK + 32 * m + 4 * sub) * sizeof(ET));
+            }
+            vn = *reinterpret_cast<const typename RV::T *>(buf + oV + (t * ROWS + (tid >> 3) * R) * sizeof(ET));
+        };
+        lds_token(0);
+        float c = 1.f;
+        for (int t = 0; t < T; ++t) {
+            f32x4 kv[NP], qv[NP];
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                kv[m] = to_f32x4<ET>(kn[m]);
+                qv[m] = to_f32x4<ET>(qn[m]);
+            }
+            const typename RV::T vt = vn;
+            const float gt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec_l), t));
+            const float bt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, beta_l), t));
+            if (t + 1 < T) lds_token(t + 1);
+            c *= gt;
+            if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the tile
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < NP; ++m) s[r][m] = c * s[r][m];
+                c = 1.f;
+            }
+            float a[R], bq[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) a[r] = bq[r] = 0.f;
+#pragma unroll
+            for (int m = 0; m < NP; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        a[r] += s[r][m][i] * kv[m][i];
+                        bq[r] += s[r][m][i] * qv[m][i];
+                    }
+                }
+            const float kq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kq_l), 8 * t));
+            const float rc = __builtin_amdgcn_rcpf(c);   // 1 ulp
+            float yo[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float ar = sum8(a[r]), br = sum8(bq[r]);
+                const float d = bt * (RV::at(vt, r) - c * ar);
+                yo[r] = (c * br + d * kq) * scale;
+                const float dc = d * rc;
+#pragma unroll
+                for (int m = 0; m < NP; ++m) s[r][m] += dc * kv[m];
+            }
+            if (sub == 0) {
+                typename RV::T yv;
+#pragma unroll
+                for (int r = 0; r < R; ++r) RV::set(yv, r, from_f32<ET>(yo[r]));
+                *reinterpret_cast<typename RV::T *>(yp + (size_t)t * vs) = yv;
+            }
+        }
+        auto store_state = [&]() {
+            const size_t row = row_of(ti);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NP; ++m)
+                    *reinterpret_cast<f32x4 *>(state_out + row + (size_t)r * DK + 32 * m) = c * s[r][m];
+        };
+        if (tn >= ntiles) {
+            store_state();
+            break;
+        }
+        // the next tile's inputs (every wave's share) and state have landed;
+        // this tile's state is stored after the wait, so that the wait does
+        // not include the time its stores take to complete
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        store_state();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NP; ++m) s[r][m] = sn[r][m];
+        ti = tn;
+    }
+}
+
+// Workgroups of seq_pipe_kernel resident on the current device at once
+// (bound by registers: the input buffers for the longest token count allowed
+// take a few percent of the LDS); 0 if the runtime cannot say.
+template <typename ET, int DK, int R>
+static long seq_pipe_resident() {
+    using L = SeqPipeCfg<ET, DK, R>;
+    static long per_dev[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (per_dev[dev] == 0) {
+        int nb = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, seq_pipe_kernel<ET, DK, R>, 256,
+                                                         2 * L::buf_bytes(kSeqPipeMaxT)) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        per_dev[dev] = (long)std::max(nb, 0) * std::max(cus, 0);
+    }
+    return per_dev[dev];
+}
+
+template <typename ET, int DK, int R>
+static hipError_t launch_seq_pipe(const FwdArgs &a, hipStream_t st, long resident) {
+    using L = SeqPipeCfg<ET, DK, R>;
+    const long ntiles = (long)a.B * a.Hv * (a.Dv / L::ROWS);
+    const int Tp = (a.T + 7) & ~7;
+    const size_t lds = 2 * (size_t)L::buf_bytes(Tp);
+    const long grid = std::min(ntiles, resident);
+    hipLaunchKernelGGL((seq_pipe_kernel<ET, DK, R>), dim3((unsigned)grid), dim3(256), lds, st,
+                       static_cast<const ET *>(a.q), static_cast<const ET *>(a.k),
+                       static_cast<const ET *>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                       static_cast<ET *>(a.y), a.T, a.Hk, a.Hv, a.Dv, a.scale, a.flags, (int)ntiles);
+    return hipGetLastError();
+}
+
 template <typename ET, int DK, int R, bool VG>
 static hipError_t launch_seq_vg(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)a.B * (unsigned)a.Hv * (unsigned)(a.Dv / (32 * R)));
@@ -322,6 +596,16 @@ static hipError_t launch_seq_inst(const FwdArgs &a, hipStream_t st) {
 template <typename ET, int DK>
 static hipError_t launch_seq_dk(const FwdArgs &a, hipStream_t st) {
     const long slots = (long)a.B * a.Hv;
+    // a few tokens on a grid of at least two tiles per resident workgroup:
+    // the persistent kernel, whose state traffic for one tile overlaps the
+    // arithmetic of another (two rows per lane: 134 registers, three waves
+    // per SIMD; four rows per lane need 218 and run slower per token)
+    if constexpr (sizeof(ET) == 2 && DK == 128) {
+        if (!(a.flags & kVectorGate) && a.T >= 1 && a.T <= kSeqPipeMaxT && a.Dv % 64 == 0) {
+            const long res = seq_pipe_resident<ET, DK, 2>();
+            if (res > 0 && slots * (a.Dv / 64) >= 2 * res) return launch_seq_pipe<ET, DK, 2>(a, st, res);
+        }
+    }
     int r = 4;
     while (r > 1 && (32 * r > a.Dv || slots * (a.Dv / (8 * r)) < kSeqMinWaves)) r >>= 1;
     switch (r) {

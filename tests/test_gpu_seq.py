@@ -184,3 +184,75 @@ def test_auto_chunk_slots(gpu_lib, B, Hk, Hv):
         sm = np.broadcast_to(mask[:, :, None, None], sr.shape)
         assert_parity(to_host_f64(y), to_host_f64(s), yr, sr, "bf16", f"auto B={B} Hk={Hk} Hv={Hv} T={T}",
                       y_mask=ym, s_mask=sm)
+
+
+def sampled_slots(B, Hv, seed, n=8):
+    """A few slots at random plus the first and the last (the last tiles of
+    a persistent workgroup's loop)."""
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((B, Hv), bool)
+    mask.reshape(-1)[rng.choice(B * Hv, n, replace=False)] = True
+    mask[0, 0] = mask[-1, -1] = True
+    return mask
+
+
+def check_sampled(y, s, inp, mask, dtype, what, **kw):
+    yr, sr = oracle_run(inp, slot_mask=mask, **kw)
+    yg, sg = to_host_f64(y), to_host_f64(s)
+    assert_parity(yg, sg, yr, sr, dtype, what,
+                  np.broadcast_to(mask[:, None, :, None], yg.shape),
+                  np.broadcast_to(mask[:, :, None, None], sg.shape))
+    assert np.isfinite(yg).all() and np.isfinite(sg).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 6, 7])
+def test_seq_persistent(gpu_lib, dtype, T):
+    """Grids of 768 slots and more with 16-bit inputs and 128-dimensional
+    keys: up to 6 tokens the persistent form of the kernel runs (each
+    workgroup walks tiles of 64 value rows, loading the next tile's inputs
+    and state while it runs the current one); 7 tokens take the other
+    form.  Both through gdn_seq_fwd and through gdn_chunk_fwd with C = 0."""
+    B, Hk, Hv = 24, 16, 32
+    inp = gi.make_inputs(B, T, Hk, Hv, 128, 128, dtype, gate="sigmoid", state_std=0.2, seed=900 + T)
+    mask = sampled_slots(B, Hv, 900 + T)
+    d = upload(inp)
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    yc, sc = gpu_lib.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], C=0)
+    torch.cuda.synchronize()
+    check_sampled(y, s, inp, mask, dtype, f"seq persistent {dtype} T={T}")
+    check_sampled(yc, sc, inp, mask, dtype, f"auto persistent {dtype} T={T}")
+
+
+@pytest.mark.parametrize("B,Hk,Hv,Dv", [(48, 16, 32, 64), (767, 1, 1, 128), (3, 256, 256, 128)],
+                         ids=["dv64_1536slots", "767slots", "768slots"])
+def test_seq_persistent_grids(gpu_lib, B, Hk, Hv, Dv):
+    """On both sides of the grid-size switch (767 and 768 slots of 128 value
+    rows), and with 64 value rows per slot; absent and in-place state."""
+    T = 4
+    inp = gi.make_inputs(B, T, Hk, Hv, 128, Dv, "bf16", gate="softplus", state_std=0.2, seed=B + Hv + Dv)
+    mask = sampled_slots(B, Hv, B * Hv)
+    d = upload(inp)
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None)
+    torch.cuda.synchronize()
+    check_sampled(y, s, inp, mask, "bf16", f"seq B={B} Hv={Hv} Dv={Dv} null state", state=False)
+    st = d["state"].clone()
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    check_sampled(y, s, inp, mask, "bf16", f"seq B={B} Hv={Hv} Dv={Dv} in place")
+
+
+@pytest.mark.parametrize("heads,gate", [("tiled", "decay"), ("grouped", "log"), ("tiled", "log")])
+def test_seq_persistent_options(gpu_lib, heads, gate):
+    """The tiled head map and log-space gates on the persistent form."""
+    B, Hk, Hv, T = 24, 16, 32, 5
+    inp = gi.make_inputs(B, T, Hk, Hv, 128, 128, "f16", gate="sigmoid", state_std=0.2, seed=77)
+    if gate == "log":
+        inp = dict(inp)
+        inp["g"] = np.log(inp["g"].astype(np.float64)).astype(np.float32)
+    mask = sampled_slots(B, Hv, 77)
+    d = upload(inp)
+    y, s = gpu_lib.seq_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], heads=heads, gate=gate)
+    torch.cuda.synchronize()
+    check_sampled(y, s, inp, mask, "f16", f"seq persistent {heads} {gate}", head_map=heads, gate=gate)
