@@ -315,10 +315,11 @@ void seq_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
 // a double buffer in LDS and the next tile's state rows into registers, so
 // that the state traffic of one tile overlaps the arithmetic of another.
 // Per token it is the arithmetic of seq_kernel above.
-// (the longest call it takes: from 8 tokens on the arithmetic per token,
-// not the state traffic, sets the time, and the kernel above is as fast;
-// at most 8, one token per group of eight lanes for k . q)
-constexpr int kSeqPipeMaxT = 6;
+// (the longest call it takes: at 8 tokens it is still a few percent ahead
+// of the kernel above, beyond that the arithmetic per token, not the state
+// traffic, sets the time; at most 8, one token per group of eight lanes
+// for k . q)
+constexpr int kSeqPipeMaxT = 8;
 static_assert(kSeqPipeMaxT <= 8, "k . q of one token per group of eight lanes");
 // s_waitcnt vmcnt(0) as an immediate (gfx9 encoding: vmcnt 0, expcnt and
 // lgkmcnt at their maxima), issued through the builtin so that the

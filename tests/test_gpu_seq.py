@@ -206,13 +206,14 @@ def check_sampled(y, s, inp, mask, dtype, what, **kw):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 6, 7])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 6, 7, 8, 9])
 def test_seq_persistent(gpu_lib, dtype, T):
     """Grids of 768 slots and more with 16-bit inputs and 128-dimensional
-    keys: up to 6 tokens the persistent form of the kernel runs (each
-    workgroup walks tiles of 64 value rows, loading the next tile's inputs
-    and state while it runs the current one); 7 tokens take the other
-    form.  Both through gdn_seq_fwd and through gdn_chunk_fwd with C = 0."""
+    keys: up to 8 tokens gdn_seq_fwd runs the persistent form of the kernel
+    (each workgroup walks tiles of 64 value rows, loading the next tile's
+    inputs and state while it runs the current one); 9 tokens take the
+    other form.  Also through gdn_chunk_fwd with C = 0 (the sequential
+    kernels up to 6 tokens, the chunked one from 7)."""
     B, Hk, Hv = 24, 16, 32
     inp = gi.make_inputs(B, T, Hk, Hv, 128, 128, dtype, gate="sigmoid", state_std=0.2, seed=900 + T)
     mask = sampled_slots(B, Hv, 900 + T)
