@@ -434,7 +434,9 @@ void seq_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
         const int hv = slot % Hv, b = slot / Hv;
         ET *yp = y + ((size_t)b * T * Hv + hv) * Dv + jt + (tid >> 3) * R;
         const char *buf = smem + (it & 1) * bufb;
-        // token t's inputs from LDS, read one token ahead
+        // token t's inputs from LDS, read at the start of the token (reading
+        // one token ahead cost a register copy of every fragment and a wave
+        // per SIMD: 124 registers let four waves share a SIMD)
         typename Vec<ET>::x4 kn[NP], qn[NP];
         typename RV::T vn;
         // the decays and betas of the tile's tokens, lane t holding token t's
@@ -463,9 +465,9 @@ void seq_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             }
             vn = *reinterpret_cast<const typename RV::T *>(buf + oV + (t * ROWS + (tid >> 3) * R) * sizeof(ET));
         };
-        lds_token(0);
         float c = 1.f;
         for (int t = 0; t < T; ++t) {
+            lds_token(t);
             f32x4 kv[NP], qv[NP];
 #pragma unroll
             for (int m = 0; m < NP; ++m) {
@@ -475,7 +477,6 @@ void seq_pipe_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             const typename RV::T vt = vn;
             const float gt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec_l), t));
             const float bt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, beta_l), t));
-            if (t + 1 < T) lds_token(t + 1);
             c *= gt;
             if (!(c >= 0x1p-24f && c <= 0x1p24f)) {   // uniform over the tile
 #pragma unroll
@@ -599,8 +600,9 @@ static hipError_t launch_seq_dk(const FwdArgs &a, hipStream_t st) {
     const long slots = (long)a.B * a.Hv;
     // a few tokens on a grid of at least two tiles per resident workgroup:
     // the persistent kernel, whose state traffic for one tile overlaps the
-    // arithmetic of another (two rows per lane: 134 registers, three waves
-    // per SIMD; four rows per lane need 218 and run slower per token)
+    // arithmetic of another (two rows per lane: about 125 registers, four
+    // waves per SIMD; four rows per lane need over 200 and run slower per
+    // token, one row per lane is slower too)
     if constexpr (sizeof(ET) == 2 && DK == 128) {
         if (!(a.flags & kVectorGate) && a.T >= 1 && a.T <= kSeqPipeMaxT && a.Dv % 64 == 0) {
             const long res = seq_pipe_resident<ET, DK, 2>();
