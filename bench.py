@@ -28,16 +28,14 @@ run about 10-20% slower).  One JSON line is printed with:
                   back-to-back steps over 8 state buffers in rotation, so
                   that every state read comes from HBM (each buffer is read
                   once every 8 steps, after some 1.9 GB of other state
-                  traffic); also each step timed alone after a cache flush,
-                  and the in-place chain;
+                  traffic), and the in-place chain;
 * ``vector_gate`` the long prefill with a decay per key dimension (g
                   [B,T,Hv,Dk], seeded U[0.95, 1) on the device): launch time
                   of the vector-gate chunk kernel (C = 32) and its HBM rate;
 * ``multi_token`` T = 2, 4, 8 tokens per call on the decode shapes: the
                   sequential kernel (``gdn_seq_fwd``), the chunked kernel at
                   C = 16 and the library's own choice (C = 0), back to back
-                  over 8 state buffers in rotation (state from HBM), and
-                  each call timed alone after a cache flush;
+                  over 8 state buffers in rotation (state from HBM);
 * ``cpu_baseline`` the float64 CPU oracle timed on the same workload (all
                   8 batch elements, all heads, all 8192 tokens: about 40
                   thread-seconds), with the thread count it used; the
@@ -218,8 +216,9 @@ def summarize_step_traffic(kind, fetch_dir, write_dir, cfetch_dir, cwrite_dir, c
 
 def decode_only(kind: str, nsteps: int):
     """The decode loop alone: 256 chained steps with the state in place, or
-    with the state ping-ponged between two buffers and a 512 MiB scratch
-    buffer read between steps (every step then reads its state from HBM)."""
+    back to back over ROTATE state buffers in rotation (every step then reads
+    its state from HBM and its output is written back while later steps
+    run)."""
     import numpy as np
     import torch
 
@@ -250,19 +249,18 @@ def decode_only(kind: str, nsteps: int):
         ev1.record(stream)
         torch.cuda.synchronize()
         us = ev0.elapsed_time(ev1) * 1e3 / nsteps
-    else:
-        scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
-        sa, sb = st0.clone(), torch.empty_like(st0)
-        tot = 0.0
+    else:                                        # rotating: every state read from HBM
+        rins = [st0.clone() for _ in range(ROTATE)]
+        routs = [torch.empty_like(st0) for _ in range(ROTATE)]
+        for i in range(nsteps):                  # warm-up pass
+            gdn.step(*toks[i], rins[i % ROTATE], state_out=routs[i % ROTATE], y=ys[i], stream=stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
         for i in range(nsteps):
-            scratch.sum()
-            ev0.record(stream)
-            gdn.step(*toks[i], sa, state_out=sb, y=ys[i], stream=stream)
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            tot += ev0.elapsed_time(ev1)
-            sa, sb = sb, sa
-        us = tot * 1e3 / nsteps
+            gdn.step(*toks[i], rins[i % ROTATE], state_out=routs[i % ROTATE], y=ys[i], stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / nsteps
     sbytes, tbytes = step_bytes(**D)
     print(json.dumps({"decode_only": kind, "steps": nsteps, "us_per_step": us,
                       "total_GBps": tbytes / (us * 1e-6) / 1e9,
@@ -302,7 +300,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
-    ap.add_argument("--decode-only", choices=["inplace", "flushed"],
+    ap.add_argument("--decode-only", choices=["inplace", "rotating"],
                     help="run only the decode loop of that kind (for counter collection)")
     ap.add_argument("--summarize-step-traffic", nargs=5, metavar=("KIND", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarise FETCH_SIZE / WRITE_SIZE of the decode step kernel for a "
@@ -380,24 +378,6 @@ def main():
         us_step = e0.elapsed_time(e1) * 1e3 / nsteps
         sbytes, tbytes = step_bytes(**D)
 
-        # Cache control: the state ping-pongs between two buffers and a
-        # 512 MiB scratch buffer is read (summed) between steps, so every step
-        # reads its state from HBM; each step is timed alone.  Reading rather
-        # than writing the scratch leaves no dirty lines in the last-level
-        # cache whose write-back would be charged to the step.
-        scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
-        sa, sb = st0.clone(), torch.empty_like(st0)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(nsteps)]
-        for i in range(nsteps):
-            scratch.sum()
-            evs[i][0].record(stream)
-            gdn.step(*toks[i], sa, state_out=sb, y=ys[i], stream=stream)
-            evs[i][1].record(stream)
-            sa, sb = sb, sa
-        torch.cuda.synchronize()
-        us_flushed = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / nsteps
-        del scratch, sa, sb, evs
         # Back-to-back steps over ROTATE state pairs: step i reads state
         # i % ROTATE and writes its own output buffer, so each state is read
         # once every ROTATE steps, after (ROTATE - 1) x 256 MiB of other state
@@ -431,13 +411,6 @@ def main():
                       "(each state read once every %d steps, after about %.1f GB of other "
                       "state traffic: from HBM), timed together with HIP events"
                       % (ROTATE, (ROTATE - 1) * 2 * sbytes / 1e9),
-            "flushed": {
-                "us_per_step": us_flushed,
-                "frac": tbytes / (us_flushed * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                "method": "state ping-pongs between two buffers; 512 MiB scratch read between "
-                          "steps; each step timed alone with HIP events (includes the launch "
-                          "and event overhead of a lone step)",
-            },
             "in_place": {
                 "us_per_step": us_step,
                 "state_GBps": sbytes / (us_step * 1e-6) / 1e9,
@@ -454,13 +427,11 @@ def main():
         D = DECODE
         dinp = gi.workload_inputs("decode")
         st0 = upload(dinp["state"], "f32")
-        scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
         rows = []
         for T in (2, 4, 8):
             tq, tk, tv = (upload(dinp[n][:, :T], "f16") for n in ("q", "k", "v"))
             tg, tb = upload(dinp["g"][:, :T], "f32"), upload(dinp["beta"][:, :T], "f32")
             ty = torch.empty((D["B"], T, D["Hv"], D["Dv"]), dtype=torch.float16, device=dev)
-            sa, sb = st0.clone(), torch.empty_like(st0)
             calls = {"seq": lambda a, b: gdn.seq_fwd(tq, tk, tv, tg, tb, a, state_out=b, y=ty,
                                                      stream=stream),
                      "chunk16": lambda a, b: gdn.chunk_fwd(tq, tk, tv, tg, tb, a, C=16, state_out=b,
@@ -471,17 +442,6 @@ def main():
             rins = [st0.clone() for _ in range(ROTATE)]
             routs = [torch.empty_like(st0) for _ in range(ROTATE)]
             for name, call in calls.items():
-                n = 16
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(n + 1)]
-                for i in range(n + 1):               # the first call warms up
-                    scratch.sum()
-                    evs[i][0].record(stream)
-                    call(sa, sb)
-                    evs[i][1].record(stream)
-                    sa, sb = sb, sa
-                torch.cuda.synchronize()
-                row[f"{name}_flushed_us"] = sum(a.elapsed_time(b) for a, b in evs[1:]) * 1e3 / n
                 # back to back over ROTATE state pairs (each state from HBM)
                 nr = 4 * ROTATE
                 for i in range(ROTATE):
@@ -501,16 +461,15 @@ def main():
             row["hbm_frac_auto"] = (sbytes + ibytes) / (row["auto_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
             row["auto_vs_best"] = row["auto_us"] / best
             rows.append(row)
-            del tq, tk, tv, tg, tb, ty, sa, sb
-        del scratch, st0
+            del tq, tk, tv, tg, tb, ty
+        del st0
         out["multi_token"] = {
             "workload": "decode shapes, T tokens per call", "B": D["B"], "Hk": D["Hk"],
             "Hv": D["Hv"], "Dk": D["Dk"], "Dv": D["Dv"], "dtype": "f16",
             "rows": rows,
-            "method": f"{{name}}_us: {4 * ROTATE} back-to-back calls over {ROTATE} state buffers in "
-                      "rotation (each state from HBM), timed together; {name}_flushed_us: state "
-                      "ping-pongs between two buffers, 512 MiB scratch read between calls, each "
-                      "call timed alone with HIP events (16 calls)",
+            "method": f"{4 * ROTATE} back-to-back calls over {ROTATE} state buffers in rotation "
+                      "(each state read from HBM once every %d calls, each output written back "
+                      "while later calls run), timed together with HIP events" % ROTATE,
             "hbm_bytes": "state read + write once per call plus q, k, v, y, g, beta of T tokens",
         }
 
