@@ -79,8 +79,17 @@ int check(const void *q, const void *k, const void *v, const float *g,
 // plus a few microseconds per token at the largest grids; the chunked kernel
 // has a higher fixed cost and a far smaller one per token, so the sequential
 // kernel wins up to a handful of tokens (more for float32 inputs, whose
-// chunked kernel runs its products at the float32 MFMA rate).
-bool seq_for(int dtype, int T) { return T <= (dtype == GDN_F32 ? 12 : 6); }
+// chunked kernel runs its products at the float32 MFMA rate).  Against the
+// per-wave chunk kernel (16-bit inputs, Dk = 128, Dv a multiple of 64; GPU
+// time of graph replays with the state read from HBM, 64..2048 slots) the
+// sequential kernel keeps only the shortest calls: up to 3 tokens on 64
+// slots, 2 up to 256, 4 up to 1024 (where the per-wave kernel's grid fills
+// the chip in two or three rounds), 1 beyond.
+bool seq_for(int dtype, int Dk, int Dv, long slots, int T, int flags) {
+    if (dtype != GDN_F32 && Dk == 128 && Dv % 64 == 0 && !(flags & gdn::kVectorGate))
+        return T <= (slots <= 64 ? 3 : slots <= 256 ? 2 : slots <= 1024 ? 4 : 1);
+    return T <= (dtype == GDN_F32 ? 12 : 6);
+}
 
 // Chunk length, from timed sweeps of GPU time (launches replayed from a HIP
 // graph) over B Hv = 2..1024, T = 2..1111, Dk/Dv in {32, 64, 128}, all
@@ -131,7 +140,7 @@ int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v,
     if (C != 0 && C != 16 && C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
-    const bool seq = C == 0 && seq_for((int)dtype, T);
+    const bool seq = C == 0 && seq_for((int)dtype, Dk, Dv, (long)B * Hv, T, flags);
     if (C == 0) C = chunk_for((int)dtype, Dk, Dv, (long)B * Hv, T);
     gdn::FwdArgs a{q, k, v, g, beta, state_in, state_out, y,
                    B, T, Hk, Hv, Dk, Dv, C, (float)(1.0 / sqrt((double)Dk)), flags};

@@ -212,8 +212,8 @@ def test_seq_persistent(gpu_lib, dtype, T):
     keys: up to 8 tokens gdn_seq_fwd runs the persistent form of the kernel
     (each workgroup walks tiles of 64 value rows, loading the next tile's
     inputs and state while it runs the current one); 9 tokens take the
-    other form.  Also through gdn_chunk_fwd with C = 0 (the sequential
-    kernels up to 6 tokens, the chunked one from 7)."""
+    other form.  Also through gdn_chunk_fwd with C = 0 (at this grid the
+    sequential kernel for one token, the per-wave chunk kernel from 2)."""
     B, Hk, Hv = 24, 16, 32
     inp = gi.make_inputs(B, T, Hk, Hv, 128, 128, dtype, gate="sigmoid", state_std=0.2, seed=900 + T)
     mask = sampled_slots(B, Hv, 900 + T)
