@@ -52,6 +52,12 @@ WRITE_SIZE of a bench run, and of a ``--copy-calibration 1024`` run), scales
 each counter by what it reads for the copy of known size, and writes the
 measured HBM bytes per chunk launch to ``profiles/`` together with a hash of
 the chunk kernel's source (the figure is only reported for that source).
+
+``--decode-only KIND`` and ``--multi-only T`` run only the decode loop, or
+only T tokens per call on the decode shapes with the library's own choice,
+for counter collection; ``--summarize-step-traffic`` and
+``--summarize-multi-traffic`` turn FETCH_SIZE / WRITE_SIZE runs of them into
+HBM bytes per dispatch in ``profiles/`` the same way.
 """
 from __future__ import annotations
 
@@ -215,6 +221,101 @@ def summarize_step_traffic(kind, fetch_dir, write_dir, cfetch_dir, cwrite_dir, c
     print(json.dumps(rec))
 
 
+WAVE_KERNEL = "chunk_wave_kernel"
+WAVE_SOURCES = ["gdn_chunk_wave.h", "gdn_chunk_wy.h", "gdn_chunk_impl.h", "gdn_chunk_dispatch.h",
+                "gdn_device.h", "gdn_internal.h", "gdn_chunk_f16.hip"]
+
+
+def wave_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in WAVE_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_prefill_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def multi_bytes(T: int) -> int:
+    """Algorithmic HBM bytes of one call of T tokens on the decode shapes: the
+    state read and written once, q, k, v, y, g, beta of T tokens."""
+    sbytes, tbytes = step_bytes(**DECODE)
+    return sbytes + (tbytes - sbytes) * T
+
+
+def summarize_multi_traffic(T, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib=1024):
+    """HBM bytes per dispatch of the per-wave chunk kernel from FETCH_SIZE /
+    WRITE_SIZE runs of ``bench.py --multi-only T``, each counter scaled by what
+    it reads for a plain copy of known size."""
+    T = int(T)
+    kib = copy_mib * 1024.0
+
+    def pick(means, needle):
+        hits = [v for k, v in means.items() if needle in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {needle!r} in counter results")
+        return max(hits)
+
+    copy_fetch = pick(_counter_means(cfetch_dir, "FETCH_SIZE"), "copyBuffer")
+    copy_write = pick(_counter_means(cwrite_dir, "WRITE_SIZE"), "copyBuffer")
+    f_scale, w_scale = kib / copy_fetch, kib / copy_write
+    fetch = pick(_counter_means(fetch_dir, "FETCH_SIZE"), WAVE_KERNEL)
+    write = pick(_counter_means(write_dir, "WRITE_SIZE"), WAVE_KERNEL)
+    rec = {
+        "kernel": f"chunk_wave_kernel<f16>, {T} tokens per call on the decode shapes "
+                  "(B=64, Hk=16, Hv=32, Dk=Dv=128), back to back over 8 rotating state buffers",
+        "T": T, "source_hash": wave_source_hash(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "copy_calibration_mib": copy_mib, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "read_bytes_per_call": fetch * f_scale * 1024,
+        "write_bytes_per_call": write * w_scale * 1024,
+        "bytes_per_call": (fetch * f_scale + write * w_scale) * 1024,
+        "algorithmic_bytes_per_call": multi_bytes(T),
+    }
+    path = os.path.join(ROOT, "profiles", f"wave_multi_token_T{T}_hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def multi_only(T: int, ncalls: int = 256):
+    """T tokens per call on the decode shapes with the library's own choice
+    (C = 0), back to back over ROTATE state buffers in rotation: every call
+    reads its state from HBM and writes it back while later calls run."""
+    import numpy as np
+    import torch
+
+    import gated_deltanet_prefill_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.load()
+    dev = torch.device("cuda", 0)
+    D = DECODE
+    dinp = gi.workload_inputs("decode")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tq, tk, tv, tg, tb = (up(dinp[n][:, :T]) for n in ("q", "k", "v", "g", "beta"))
+    st0 = up(dinp["state"])
+    ty = torch.empty((D["B"], T, D["Hv"], D["Dv"]), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rins = [st0.clone() for _ in range(ROTATE)]
+    routs = [torch.empty_like(st0) for _ in range(ROTATE)]
+    call = lambda i: gdn.chunk_fwd(tq, tk, tv, tg, tb, rins[i % ROTATE], C=0, state_out=routs[i % ROTATE],
+                                   y=ty, stream=stream)
+    for i in range(ROTATE):                      # warm-up pass
+        call(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(ncalls):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / ncalls
+    nbytes = multi_bytes(T)
+    print(json.dumps({"multi_only": T, "calls": ncalls, "us_per_call": us,
+                      "total_GBps": nbytes / (us * 1e-6) / 1e9,
+                      "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
+
+
 def decode_only(kind: str, nsteps: int):
     """The decode loop alone: 256 chained steps with the state in place, or
     back to back over ROTATE state buffers in rotation (every step then reads
@@ -303,6 +404,12 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     ap.add_argument("--decode-only", choices=["inplace", "rotating"],
                     help="run only the decode loop of that kind (for counter collection)")
+    ap.add_argument("--multi-only", type=int, choices=[2, 4, 8, 16],
+                    help="run only T tokens per call on the decode shapes, back to back over rotating "
+                         "state buffers (for counter collection)")
+    ap.add_argument("--summarize-multi-traffic", nargs=5, metavar=("T", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="summarise FETCH_SIZE / WRITE_SIZE of the per-wave chunk kernel for a "
+                         "--multi-only T run")
     ap.add_argument("--summarize-step-traffic", nargs=5, metavar=("KIND", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarise FETCH_SIZE / WRITE_SIZE of the decode step kernel for a "
                          "--decode-only KIND run")
@@ -312,6 +419,9 @@ def main():
         return
     if args.summarize_step_traffic:
         summarize_step_traffic(*args.summarize_step_traffic)
+        return
+    if args.summarize_multi_traffic:
+        summarize_multi_traffic(*args.summarize_multi_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
@@ -323,6 +433,9 @@ def main():
         return
     if args.decode_only:
         decode_only(args.decode_only, args.decode_steps)
+        return
+    if args.multi_only:
+        multi_only(args.multi_only)
         return
 
     import numpy as np
