@@ -1,6 +1,6 @@
 // gdn_chunk_vg_f16.hip -- per-key-dimension-gate chunk kernel instantiations for f16 q/k/v/y.
-#include "gdn_chunk_vg.h"
+#include "gdn_chunk_vgp.h"
 
 namespace gdn {
-hipError_t launch_chunk_vg_f16(const FwdArgs &a, hipStream_t s) { return launch_chunk_vg_typed<_Float16>(a, s); }
+hipError_t launch_chunk_vg_f16(const FwdArgs &a, hipStream_t s) { return launch_chunk_vg_any<_Float16>(a, s); }
 }  // namespace gdn
