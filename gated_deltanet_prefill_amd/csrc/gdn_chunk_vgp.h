@@ -37,6 +37,71 @@
 
 namespace gdn {
 
+// DPP move that writes zero where a lane has no source: unlike a move that
+// keeps an old value, the compiler folds it into the consuming multiply.
+template <int CTRL>
+__device__ __forceinline__ float dppz(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// Per-lane decay scales of the four within-block levels, for lane x of a
+// 16-token block (the decays g of token x, four key dimensions).  Level l
+// pairs a token j in the lower half of a 2^(l+1)-token segment with a token t
+// in its upper half; their decay product over (j, t] is e_l(j) p_l(t), where
+// p_l(t) runs from the start of t's 2^l-token segment to t and e_l(j) from
+// j + 1 to the end of j's.  A lane is only ever the t side (upper half) or
+// the j side (lower half) of a level, so one scale serves both MFMA
+// operands: s[l] = p_l on the upper half, e_l on the lower.  Also the
+// block's prefix P16 (tokens 0..x) and suffix S16 (x + 1..15).  Lanes
+// without a DPP source read zero, and only where the select discards it.
+struct VgScales {
+    f32x4 s[4];
+    f32x4 p16, s16;
+};
+
+__device__ __forceinline__ VgScales vg_scales(f32x4 g, int x) {
+    const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+    auto sel = [](bool c, f32x4 a, f32x4 b) { return c ? a : b; };
+    // 0x111 row_shr:1, 0x101 row_shl:1, 0x55 / 0xaa / 0xff / 0x00 quad lane
+    // 1 / 2 / 3 / 0, 0x114 / 0x104 row_shr:4 / row_shl:4, 0x15N row_newbcast:N
+    f32x4 t, u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = g[c] * dppz<0x111>(g[c]);
+    const f32x4 p1 = sel(x & 1, t, g);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = p1[c] * dppz<0x55>(p1[c]);
+    const f32x4 p2 = sel(x & 2, t, p1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { u[c] = dppz<0xff>(p2[c]); t[c] = p2[c] * dppz<0x114>(u[c]); }
+    const f32x4 p3 = sel(x & 4, t, p2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = p3[c] * dppz<0x157>(p3[c]);
+    const f32x4 p4 = sel(x & 8, t, p3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = dppz<0x101>(g[c]);
+    const f32x4 e1 = sel(x & 1, one, t);
+    f32x4 sg = g * e1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = e1[c] * dppz<0xaa>(sg[c]);
+    const f32x4 e2 = sel(x & 2, e1, t);
+    sg = g * e2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { u[c] = dppz<0x00>(sg[c]); t[c] = e2[c] * dppz<0x104>(u[c]); }
+    const f32x4 e3 = sel(x & 4, e2, t);
+    sg = g * e3;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = e3[c] * dppz<0x158>(sg[c]);
+    const f32x4 e4 = sel(x & 8, e3, t);
+    VgScales r;
+    r.s[0] = sel(x & 1, g, one);
+    r.s[1] = sel(x & 2, p1, e1);
+    r.s[2] = sel(x & 4, p2, e2);
+    r.s[3] = sel(x & 8, p3, e3);
+    r.p16 = p4;
+    r.s16 = e4;
+    return r;
+}
+
 template <typename ET>
 struct VgpCfg {
     static constexpr int DK = 128, DV = 128, C = 32, NB = 2, NBT = 2, NBK = 8;
@@ -331,16 +396,16 @@ void chunk_vgp_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     kx[h] = valid ? cur.kk[h] : z4;
                     qx[h] = valid ? cur.qq[h] : z4;
                     const f32x4 kf = to_f32x4<ET>(kx[h]), qf = to_f32x4<ET>(qx[h]);
-                    const SegScan sc = seg_scan(g4, x);
+                    const VgScales sc = vg_scales(g4, x);
 #pragma unroll
                     for (int lv = 0; lv < 4; ++lv) {
-                        const X4 ka = cvt4<ET>(kf * sc.e[lv]);
-                        kk[lv] = mfma(ka, cvt4<ET>(kf * sc.p[lv]), kk[lv]);
-                        qk[lv] = mfma(ka, cvt4<ET>(qf * sc.p[lv]), qk[lv]);
+                        const X4 ku = cvt4<ET>(kf * sc.s[lv]);
+                        kk[lv] = mfma(ku, ku, kk[lv]);
+                        qk[lv] = mfma(ku, cvt4<ET>(qf * sc.s[lv]), qk[lv]);
                     }
                     q0 = mfma(kx[h], qx[h], q0);
-                    P16[h] = sc.p[4];
-                    S16[h] = sc.e[4];
+                    P16[h] = sc.p16;
+                    S16[h] = sc.s16;
                     if (x == 15) *reinterpret_cast<f32x4 *>(sBT + bt * DK + i0) = P16[h];
                     if (bt == 0) {
                         // block 0: G = P16; K diag(S16) for the cross-block tile
@@ -353,17 +418,20 @@ void chunk_vgp_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     }
                 }
                 // keep each entry's own level (the highest bit in which the
-                // in-block indices of t and j differ): a weighted sum, no branches
+                // in-block indices of t and j differ); zero above the diagonal
                 f32x4 za, zo;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int jl = 4 * qd + r, d = jl ^ x;
-                    const float w3 = d >= 8 ? 1.f : 0.f, w2 = (d >= 4 && d < 8) ? 1.f : 0.f,
-                                w1 = (d >= 2 && d < 4) ? 1.f : 0.f, w0 = d == 1 ? 1.f : 0.f;
-                    const float lower = jl < x ? 1.f : 0.f, diag = jl == x ? 1.f : 0.f;
-                    za[r] = lower * (w0 * kk[0][r] + w1 * kk[1][r] + w2 * kk[2][r] + w3 * kk[3][r]);
-                    zo[r] = lower * (w0 * qk[0][r] + w1 * qk[1][r] + w2 * qk[2][r] + w3 * qk[3][r]) +
-                            diag * q0[r];
+                    float zk = kk[0][r], zq = qk[0][r];
+                    zk = d >= 2 ? kk[1][r] : zk;
+                    zq = d >= 2 ? qk[1][r] : zq;
+                    zk = d >= 4 ? kk[2][r] : zk;
+                    zq = d >= 4 ? qk[2][r] : zq;
+                    zk = d >= 8 ? kk[3][r] : zk;
+                    zq = d >= 8 ? qk[3][r] : zq;
+                    za[r] = jl < x ? zk : 0.f;
+                    zo[r] = jl < x ? zq : (jl == x ? q0[r] : 0.f);
                 }
                 f32x4 *part = reinterpret_cast<f32x4 *>(smem + L::oPd) + (pw * 2) * 64 + lane;
                 part[0] = za;
@@ -372,10 +440,12 @@ void chunk_vgp_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                     reinterpret_cast<float *>(smem + P + L::pB)[tok] = valid ? cur.be : 0.f;
             }
             // the last steps of chunk it - 1: its cross-block tile (from the
-            // partials its phase b left), its diagonal inverses
+            // partials its phase b left), its diagonal inverses.  The waves of
+            // block 0 finish their scans first (the older wave of each SIMD
+            // issues first), so they take this work, one piece per SIMD.
             if (fin) {
                 const unsigned PP = parity(it - 1);
-                if (pw == 5) {
+                if (pw == 3) {
                     f32x4 zk = zero4(), zq = zero4();
 #pragma unroll
                     for (int pp = 0; pp < 4; ++pp) {
@@ -383,16 +453,18 @@ void chunk_vgp_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         zk += px[0];
                         zq += px[64];
                     }
-                    const float bv = reinterpret_cast<const float *>(smem + PP + L::pB)[tok];
-                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(smem + PP + L::pAn) + tok * LDCF + 4 * qd) =
+                    const int t1 = 16 + x;
+                    const float bv = reinterpret_cast<const float *>(smem + PP + L::pB)[t1];
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(smem + PP + L::pAn) + t1 * LDCF + 4 * qd) =
                         zk * (-bv);
-                    st4<ET>(reinterpret_cast<ET *>(smem + PP + L::pQKR) + tok * LDC + 4 * qd, cvt4<ET>(zq * scale));
+                    st4<ET>(reinterpret_cast<ET *>(smem + PP + L::pQKR) + t1 * LDC + 4 * qd, cvt4<ET>(zq * scale));
                 }
-                if (kq == 0) {
-                    // T_bb = (I + A_bb)^-1: four lanes per column c, lane part pt
-                    // holding rows pt, pt + 4, pt + 8, pt + 12; once x_j is final
-                    // (in part j % 4), every later row subtracts A[i][j] x_j
-                    const int base = 16 * bt;
+                if (pw == 0 || pw == 2) {
+                    // T_bb = (I + A_bb)^-1 of block pw / 2: four lanes per column
+                    // c, lane part pt holding rows pt, pt + 4, pt + 8, pt + 12;
+                    // once x_j is final (in part j % 4), every later row
+                    // subtracts A[i][j] x_j
+                    const int base = 8 * pw;
                     const int pt = lane & 3, c = ((lane >> 4) << 2) | ((lane >> 2) & 3);
                     f32x4 arow[4][4];
 #pragma unroll
@@ -425,20 +497,24 @@ void chunk_vgp_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
             // ---------------- phase b: diagonal tiles of chunk it, cross-block
             // partials, the scaled K and Q that need the other block's totals
             if (work) {
-                if (kq == 0) {
+                if (pw == 1 || pw == 3) {
+                    // the diagonal tile of block db = pw / 2: partial sums of
+                    // its four key quarters, rows scaled by beta (zero past
+                    // the end)
+                    const int db = pw >> 1, tb = 16 * db + x;
                     f32x4 a = zero4(), o = zero4();
 #pragma unroll
                     for (int pp = 0; pp < 4; ++pp) {
-                        const f32x4 *pin = reinterpret_cast<const f32x4 *>(smem + L::oPd) + ((4 * bt + pp) * 2) * 64 + lane;
+                        const f32x4 *pin = reinterpret_cast<const f32x4 *>(smem + L::oPd) + ((4 * db + pp) * 2) * 64 + lane;
                         a += pin[0];
                         o += pin[64];
                     }
-                    a *= valid ? cur.be : 0.f;
+                    a *= reinterpret_cast<const float *>(smem + P + L::pB)[tb];
                     o *= scale;
-                    const int j0 = 16 * bt + 4 * qd;
-                    *reinterpret_cast<f32x4 *>(sAn + tok * LDCF + j0) = -a;
-                    st4<ET>(sQKR + tok * LDC + j0, cvt4<ET>(o));
-                    *reinterpret_cast<f32x4 *>(sAd + tok * LDD + 4 * qd) = a;
+                    const int j0 = 16 * db + 4 * qd;
+                    *reinterpret_cast<f32x4 *>(sAn + tb * LDCF + j0) = -a;
+                    st4<ET>(sQKR + tb * LDC + j0, cvt4<ET>(o));
+                    *reinterpret_cast<f32x4 *>(sAd + tb * LDD + 4 * qd) = a;
                 }
                 if (bt == 1) {
                     // cross-block tile (j in block 0, t = this wave's token):
