@@ -68,6 +68,22 @@ __device__ __forceinline__ typename Vec<T>::x4 cvt4(f32x4 a) {
     return r;
 }
 
+// bfloat16: converted in pairs and packed through 32-bit words.  Written
+// element by element, a result that feeds a matrix-core operand is
+// converted one value per instruction and repacked with byte permutes
+// (three times the vector-ALU work); pairs keep one packed conversion per
+// two values.  Rounding is the same (to nearest even).
+template <>
+__device__ __forceinline__ bf16x4 cvt4<__bf16>(f32x4 a) {
+    typedef float f32x2_ __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x2_ __attribute__((ext_vector_type(2)));
+    const bf16x2_ lo = __builtin_convertvector(f32x2_{a[0], a[1]}, bf16x2_);
+    const bf16x2_ hi = __builtin_convertvector(f32x2_{a[2], a[3]}, bf16x2_);
+    const u32x2_ w = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    return __builtin_bit_cast(bf16x4, w);
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 to_f32x4(typename Vec<T>::x4 a) {
     f32x4 r;
