@@ -486,7 +486,7 @@ def main():
         vg_bytes = prefill_bytes(**P) + 4 * P["B"] * P["T"] * P["Hv"] * (P["Dk"] - 1)
         out["vector_gate"] = {
             "workload": "long prefill with a decay per key dimension (g [B,T,Hv,Dk] f32, U[0.95,1))",
-            "kernel": "chunk_vg_kernel<bf16,128,128,32>", "C": 32,
+            "kernel": "chunk_vgp_kernel<bf16>", "C": 32,
             "us_per_launch": us_vg, "tokens_per_s": P["B"] * P["T"] / (us_vg * 1e-6),
             "hbm_GBps": vg_bytes / (us_vg * 1e-6) / 1e9,
             "hbm_frac": vg_bytes / (us_vg * 1e-6) / 1e9 / HBM_PEAK_GBS,

@@ -158,7 +158,7 @@ __device__ __forceinline__ typename Vec<ET>::x4 frag_col(const ET *m, int ld, in
 // Broadcast lane K of every group of four lanes to the group (DPP quad_perm).
 template <int K>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xf, 0xf, true));
 }
 
 // Value of the lane S below / above within each row of 16 lanes (DPP
