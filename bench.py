@@ -32,7 +32,8 @@ W = 5.  One JSON line is printed with:
                   traffic), and the in-place chain;
 * ``vector_gate`` the long prefill with a decay per key dimension (g
                   [B,T,Hv,Dk], seeded U[0.95, 1) on the device): launch time
-                  of the vector-gate chunk kernel (C = 32) and its HBM rate;
+                  of the pipelined vector-gate chunk kernel (C = 32; 5
+                  untimed launches, then 20 timed) and its HBM rate;
 * ``multi_token`` T = 2, 4, 8 tokens per call on the decode shapes: the
                   sequential kernel (``gdn_seq_fwd``), the chunked kernel at
                   C = 16 and the library's own choice (C = 0), back to back
@@ -473,7 +474,8 @@ def main():
         gvec = 0.95 + 0.05 * torch.rand((P["B"], P["T"], P["Hv"], P["Dk"]), generator=gen, device=dev)
         s_vg = torch.empty_like(s_in)
         call = lambda: gdn.chunk_fwd(q, k, v, gvec, beta, s_in, C=32, state_out=s_vg, y=y, stream=stream)
-        call()
+        for _ in range(5):
+            call()
         torch.cuda.synchronize()
         n = 20
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
