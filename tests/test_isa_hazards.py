@@ -77,9 +77,13 @@ def mixed_chains(asm: str):
 
 
 def _compile(src):
+    # the per-source flags of the library build (the scheduler choice of the
+    # pipelined kernel's four-slice units), so that the checked code is the
+    # code that ships
+    from gated_deltanet_prefill_amd.build import EXTRA
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-x", "hip",
-           "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
+           "-Xclang", "-packed-fp32-ops", *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"),
+           "-x", "hip", "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return r.stdout
@@ -108,6 +112,7 @@ def test_scan_finds_a_planted_chain():
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_no_close_mixed_shape_accumulator_chains():
     srcs = ["gdn_chunk_bf16.hip", "gdn_chunk_f16.hip", "gdn_chunk_f32.hip",
+            "gdn_chunk_wy2_bf16.hip", "gdn_chunk_wy2_f16.hip",
             "gdn_chunk_vg_bf16.hip", "gdn_chunk_vg_f16.hip", "gdn_chunk_vg_f32.hip"]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         asms = list(ex.map(_compile, srcs))
