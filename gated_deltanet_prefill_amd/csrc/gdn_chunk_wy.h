@@ -50,6 +50,10 @@
 //            prep:  the first blocks of T_{n+1} below the diagonal; gate
 //                   products of chunk n+2; load Q_{n+1}, V_{n+1}
 //
+// The decay ratios of the four diagonal 16x16 tiles, which the prep waves
+// form for their K K^T tiles, are kept in LDS (lane order, two chunks by
+// parity) for the Q K^T diagonal tiles of the same chunk.
+//
 // LDS layouts.  K and Q have 256-byte token rows (keys along the row); the
 // 16-byte unit u of row t sits at u ^ kq_swz(t).  QKR has 128-byte rows, unit
 // u of row t at u ^ ((t / 2) % 8), and column j = 32 s + 16 h + 4 q + r at
@@ -109,7 +113,9 @@ struct WyCfg {
     static constexpr unsigned NV = 7 * C;                 // floats per gate-vector set
     static constexpr unsigned oVec = oTU + 2 * TBUF;      // 3 gate-vector sets
     static constexpr unsigned oGB = oVec + 3 * NV * 4;    // g, beta of two chunks, as loaded
-    static constexpr unsigned BYTES = oGB + 2 * 2 * C * 4;
+    // decay ratios of the four diagonal tiles (lane order), two chunks
+    static constexpr unsigned oRd = oGB + 2 * 2 * C * 4;
+    static constexpr unsigned BYTES = oRd + 2 * NBT * 1024;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -454,10 +460,12 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
     // QKR = R (Q K^T) / sqrt(Dk), lower including the diagonal, from tile
     // (ib, jb) of Q K^T in registers (lane (x, qd): t = 16 ib + x, j = 16 jb
     // + 4 qd + r)
-    auto store_qkr = [&](const float *gv, int ib, int jb, f32x4 acc) {
+    auto store_qkr = [&](const float *gv, int c, int ib, int jb, f32x4 acc) {
         const unsigned lA = f_lA();
         if (ib == jb) {
-            const f32x4 R = diag_ratio(gv, ib);
+            // the ratios the prep wave of this diagonal block formed for its
+            // K K^T tile of the same chunk (same lanes, same values)
+            const f32x4 R = *reinterpret_cast<const f32x4 *>(smem + L::oRd + (c & 1) * NBT * 1024 + ib * 1024 + 16 * lane);
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = (4 * qd + r <= x) ? scale * (R[r] * acc[r]) : 0.f;
@@ -588,7 +596,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         __builtin_amdgcn_sched_barrier(0x2);
                     }
 #pragma unroll
-                    for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
+                    for (int i = 0; i < nt; ++i) store_qkr(gv, n, TL.t[i].ib, TL.t[i].jb, acc[i]);
                 };
                 with_wave<NSW>(w, products);
                 // the right-hand side E = V - G M in two 16-bit parts: V as
@@ -786,6 +794,8 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                         const float bt = gv[kVb * C + 16 * ib + x];
                         if (ib == jb) {
                             const f32x4 R = diag_ratio(gv, ib);
+                            // kept for the Q K^T tile (ib, ib) of this chunk
+                            *reinterpret_cast<f32x4 *>(smem + L::oRd + (m & 1) * NBT * 1024 + ib * 1024 + 16 * lane) = R;
                             f32x4 a;
 #pragma unroll
                             for (int r = 0; r < 4; ++r) a[r] = (4 * qd + r < x) ? bt * (R[r] * acc[i][r]) : 0.f;
@@ -865,7 +875,7 @@ void chunk_wy_kernel(const ET *__restrict__ q, const ET *__restrict__ k,
                                               lds8<ET>(smem, L::oQ + lo + 4096 * TL.t[i].ib), acc[i]);
                         }
 #pragma unroll
-                        for (int i = 0; i < nt; ++i) store_qkr(gv, TL.t[i].ib, TL.t[i].jb, acc[i]);
+                        for (int i = 0; i < nt; ++i) store_qkr(gv, n, TL.t[i].ib, TL.t[i].jb, acc[i]);
                         }
                     };
                     with_wave<L::NP>(p, qk_tiles);
